@@ -1,0 +1,324 @@
+"""Pin checks for the CPU oracle, written against an oracle namespace.
+
+Each ``check_*`` function raises AssertionError when the oracle it is given
+disagrees with something fixed independently of it: values worked by hand
+(``tests/golden/``), brute force with Python loops, a library routine
+(``torch``'s scaled-dot-product attention), mpmath at 50 digits, closed forms
+and invariances. ``test_oracle.py`` runs them on the real oracle, and
+``test_oracle_mutants.py`` runs them on copies of the oracle with planted
+mistakes, each of which must be caught by at least one check.
+
+Nothing here imports the HIP library.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+def _rand(shape, seed):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=torch.float64).numpy()
+
+
+# ---------------------------------------------------------------- brute force
+def brute_visible(f, frames, window, ref_frame):
+    """Independent restatement of the mask rule with explicit loops."""
+    out = []
+    for g in range(frames):
+        if abs(g - f) <= window or g == ref_frame:
+            out.append(g)
+    return out
+
+
+def brute_attention(q, k, v, frames, t, window, ref_frame, scale):
+    """Masked softmax attention with Python loops and math.exp (tiny inputs)."""
+    bsz, heads, n, d = q.shape
+    o = np.zeros_like(q)
+    for b in range(bsz):
+        for h in range(heads):
+            for i in range(n):
+                vis = brute_visible(i // t, frames, window, ref_frame)
+                keys = [j for j in range(n) if (j // t) in vis]
+                s = [scale * sum(q[b, h, i, c] * k[b, h, j, c] for c in range(d)) for j in keys]
+                m = max(s)
+                w = [math.exp(x - m) for x in s]
+                z = sum(w)
+                for c in range(d):
+                    o[b, h, i, c] = sum(wj * v[b, h, j, c] for wj, j in zip(w, keys)) / z
+    return o
+
+
+def check_golden_attention(orc):
+    g = _load("attention_hand_worked.json")
+    q = np.array(g["q"])[None, None]
+    k = np.array(g["k"])[None, None]
+    v = np.array(g["v"])[None, None]
+    for case in g["cases"]:
+        o = orc.attention(q, k, v, case["frames"], case["tokens_per_frame"], case["window"],
+                          case["ref_frame"], g["scale"])
+        np.testing.assert_allclose(o[0, 0], np.array(case["o"]), rtol=0, atol=1e-12)
+
+
+def check_golden_plans(orc):
+    for name in ("plan_5x80_w1_r0.json", "plan_5x80_w1_r0_bq16.json"):
+        g = _load(name)
+        info, row_ptr, col_idx = orc.plan(g["frames"], g["tokens_per_frame"], g["window"],
+                                          g["ref_frame"], g["block_q"], g["block_k"])
+        for key in ("n_qblocks", "n_kblocks", "nnz", "block_q", "block_k"):
+            assert info[key] == g[key], (name, key)
+        assert row_ptr.tolist() == g["row_ptr"], name
+        assert col_idx.tolist() == g["col_idx"], name
+
+
+BRUTE_CASES = [
+    # frames, T, D, window, ref
+    (1, 16, 8, 0, 0),
+    (2, 16, 8, 1, 1),
+    (3, 16, 8, 0, 0),
+    (4, 16, 16, 1, 0),
+    (4, 32, 8, 2, 3),
+    (4, 16, 8, 5, 3),
+    (3, 32, 16, 0, 2),
+    (4, 16, 8, 1, 2),
+]
+
+
+def check_brute_force(orc, cases=BRUTE_CASES):
+    for idx, (frames, t, d, w, r) in enumerate(cases):
+        n = frames * t
+        q, k, v = (_rand((1, 2, n, d), 100 * idx + s) for s in range(3))
+        scale = 1.0 / math.sqrt(d)
+        ref = brute_attention(q, k, v, frames, t, w, r, scale)
+        got = orc.attention(q, k, v, frames, t, w, r, scale)
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+        rows = [(0, 1, 0), (0, 0, n - 1), (0, 1, n // 2)]
+        got_rows = orc.attention_rows(q, k, v, rows, frames, t, w, r, scale)
+        for x, (b, h, i) in enumerate(rows):
+            np.testing.assert_allclose(got_rows[x], ref[b, h, i], rtol=0, atol=1e-12)
+
+
+def check_weights(orc):
+    frames, t, d, w, r = 4, 16, 8, 1, 2
+    n = frames * t
+    q, k = _rand((1, 2, n, d), 7), _rand((1, 2, n, d), 8)
+    p = orc.attention_weights(q, k, frames, t, w, r, 1.0 / math.sqrt(d))
+    np.testing.assert_allclose(p.sum(-1), 1.0, rtol=0, atol=1e-12)
+    for i in range(n):
+        vis = brute_visible(i // t, frames, w, r)
+        for j in range(n):
+            if (j // t) not in vis:
+                assert p[0, 0, i, j] == 0.0 and p[0, 1, i, j] == 0.0
+            else:
+                assert p[0, 0, i, j] > 0.0
+
+
+def check_dense_limit(orc):
+    """Window >= F - 1 makes the mask all-ones: plain attention (torch, fp64)."""
+    frames, t, d = 3, 16, 16
+    n = frames * t
+    q, k, v = (_rand((1, 2, n, d), 20 + s) for s in range(3))
+    scale = 1.0 / math.sqrt(d)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), scale=scale).numpy()
+    for w in (frames - 1, frames + 4):
+        got = orc.attention(q, k, v, frames, t, w, 1, scale)
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    info, row_ptr, col_idx = orc.plan(frames, t, frames - 1, 0, 16, 16)
+    assert info["nnz"] == info["n_qblocks"] * info["n_kblocks"]
+
+
+def check_closed_forms(orc):
+    frames, t, d, w, r = 5, 16, 5, 1, 0
+    n = frames * t
+    scale = 0.25
+    rng_v = _rand((1, 1, n, d), 30)
+    zero_q = np.zeros((1, 1, n, d))
+    k = _rand((1, 1, n, d), 31)
+    # q = 0: uniform weights over the visible keys -> mean of v over them; B_i = 0
+    o = orc.attention(zero_q, k, rng_v, frames, t, w, r, scale)
+    for i in range(n):
+        vis = brute_visible(i // t, frames, w, r)
+        keys = [j for j in range(n) if j // t in vis]
+        np.testing.assert_allclose(o[0, 0, i], rng_v[0, 0, keys].mean(0), rtol=0, atol=1e-12)
+    bnd = orc.bounds(zero_q, k, frames, t, w, r, scale, 16, 16)
+    assert np.all(bnd["row_bound"] == 0.0) and np.all(bnd["qnorm"] == 0.0)
+    # constant v rows -> that constant
+    q = _rand((1, 1, n, d), 32)
+    const_v = np.broadcast_to(np.array([1.5, -2.0, 0.0, 3.25, 7.0]), (1, 1, n, d)).copy()
+    o = orc.attention(q, k, const_v, frames, t, w, r, scale)
+    np.testing.assert_allclose(o, const_v, rtol=0, atol=1e-12)
+    # frame-indicator v: column c = [frame(j) == c] -> attention mass per frame
+    ind_v = np.zeros((1, 1, n, frames))
+    for j in range(n):
+        ind_v[0, 0, j, j // t] = 1.0
+    o = orc.attention(q[..., :frames], k[..., :frames], ind_v, frames, t, w, r, scale)
+    np.testing.assert_allclose(o.sum(-1), 1.0, rtol=0, atol=1e-12)
+    for i in range(n):
+        vis = brute_visible(i // t, frames, w, r)
+        for c in range(frames):
+            if c not in vis:
+                assert o[0, 0, i, c] == 0.0
+    o0 = orc.attention(zero_q[..., :frames], k[..., :frames], ind_v, frames, t, w, r, scale)
+    for i in range(n):
+        vis = brute_visible(i // t, frames, w, r)
+        for c in vis:
+            assert abs(o0[0, 0, i, c] - 1.0 / len(vis)) < 1e-12
+
+
+def check_bound_shift_exact(orc):
+    """Norm-bound softmax equals max-subtract softmax: mpmath at 50 digits on a
+    tiny case (the identity itself), then the oracle's fp64 bound-shift form."""
+    import mpmath
+    mpmath.mp.dps = 50
+    frames, t, d, w, r = 3, 2, 4, 0, 0
+    n = frames * t
+    q, k, v = (_rand((1, 1, n, d), 40 + s) for s in range(3))
+    scale = 0.5
+    bnd = orc.bounds(np.zeros((1, 1, 16 * frames, d)), np.zeros((1, 1, 16 * frames, d)),
+                     frames, 16, w, r, scale, 16, 16)      # exercised for shape only
+    assert bnd["bmax"].shape == (1, 1)
+    for i in range(n):
+        vis = brute_visible(i // t, frames, w, r)
+        keys = [j for j in range(n) if j // t in vis]
+        s = [mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(q[0, 0, i, c]) * mpmath.mpf(k[0, 0, j, c])
+                                             for c in range(d)) for j in keys]
+        qn = mpmath.sqrt(mpmath.fsum(mpmath.mpf(x) ** 2 for x in q[0, 0, i]))
+        kn = max(mpmath.sqrt(mpmath.fsum(mpmath.mpf(x) ** 2 for x in k[0, 0, j])) for j in keys)
+        bound = mpmath.mpf(scale) * qn * kn
+        assert all(x <= bound for x in s)
+        m = max(s)
+        for c in range(d):
+            a = mpmath.fsum(mpmath.exp(x - m) * mpmath.mpf(v[0, 0, j, c]) for x, j in zip(s, keys)) \
+                / mpmath.fsum(mpmath.exp(x - m) for x in s)
+            b = mpmath.fsum(mpmath.exp(x - bound) * mpmath.mpf(v[0, 0, j, c]) for x, j in zip(s, keys)) \
+                / mpmath.fsum(mpmath.exp(x - bound) for x in s)
+            assert abs(a - b) < mpmath.mpf("1e-40")
+    # fp64: the oracle's bound-shift form against its max-subtract form
+    frames, t, d, w, r = 4, 16, 16, 1, 0
+    n = frames * t
+    q, k, v = (_rand((1, 2, n, d), 50 + s) for s in range(3))
+    scale = 1.0 / math.sqrt(d)
+    bnd = orc.bounds(q, k, frames, t, w, r, scale, 16, 16)
+    a = orc.attention(q, k, v, frames, t, w, r, scale)
+    b = orc.attention_bound_shift(q, k, v, frames, t, w, r, scale, bnd["row_bound"])
+    np.testing.assert_allclose(b, a, rtol=0, atol=1e-12)
+
+
+def check_cauchy_schwarz(orc):
+    frames, t, d, w, r = 4, 32, 8, 1, 3
+    n = frames * t
+    q, k = _rand((1, 2, n, d), 60), _rand((1, 2, n, d), 61)
+    k[0, 1, 5] *= 30.0          # one long key in frame 0
+    scale = 0.3
+    mask = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        for j in range(n):
+            mask[i, j] = (j // t) in brute_visible(i // t, frames, w, r)
+    s = scale * np.einsum("bhid,bhjd->bhij", q, k)
+    ref_bound = None
+    for bq, bk in ((16, 16), (16, 32), (32, 16), (32, 32)):
+        bnd = orc.bounds(q, k, frames, t, w, r, scale, bq, bk)
+        rb = bnd["row_bound"]
+        assert np.all(np.where(mask, s <= rb[..., None] * (1 + 1e-12), True))
+        # tight: the row bound uses the largest visible key norm, no other
+        qn = np.sqrt((q * q).sum(-1))
+        kn = np.sqrt((k * k).sum(-1))
+        want = np.empty_like(qn)
+        for i in range(n):
+            want[:, :, i] = scale * qn[:, :, i] * np.where(mask[i], kn, 0.0).max(-1)
+        np.testing.assert_allclose(rb, want, rtol=1e-14, atol=0)
+        if ref_bound is not None:
+            np.testing.assert_array_equal(rb, ref_bound)
+        ref_bound = rb
+        np.testing.assert_allclose(bnd["bmax"], want.max(-1), rtol=1e-14, atol=0)
+        np.testing.assert_allclose(
+            bnd["kmax"], kn.reshape(1, 2, n // bk, bk).max(-1), rtol=1e-15, atol=0)
+    np.testing.assert_allclose(orc.row_bound_by_frames(q, k, frames, t, w, r, scale), ref_bound,
+                               rtol=1e-14, atol=0)
+    # eligibility: head 1 holds the long key, so its bound exceeds a limit head 0 meets
+    limit = float(ref_bound[0, 0].max()) * 1.01
+    bnd = orc.bounds(q, k, frames, t, w, r, scale, 16, 16, bound_limit=limit)
+    assert bnd["eligible"].tolist() == [[1, 0]]
+
+
+def plan_nnz_closed_form(frames, t, w, r, bq, bk):
+    pairs = 0
+    for f in range(frames):
+        pairs += len(brute_visible(f, frames, w, r))
+    return pairs * (t // bq) * (t // bk)
+
+
+def check_plan_closed_form(orc):
+    for frames, t, w, r in ((5, 80, 1, 0), (21, 1200, 1, 0), (13, 3600, 2, 0), (14, 1200, 13, 0),
+                            (6, 48, 2, 5), (3, 16, 0, 1), (1, 32, 0, 0)):
+        sizes = [b for b in range(16, t + 1, 16) if t % b == 0]
+        if frames * t > 4000:       # brute force costs ~N^2 per plan: two plans only
+            combos = [orc.auto_block_sizes(t), (sizes[-1], sizes[0])]
+        else:
+            picks = sorted({sizes[0], sizes[-1], sizes[len(sizes) // 2]})
+            combos = list(itertools.product(picks, picks))
+        for bq, bk in combos:
+            info, row_ptr, col_idx = orc.plan(frames, t, w, r, bq, bk)
+            assert info["nnz"] == plan_nnz_closed_form(frames, t, w, r, bq, bk)
+            assert row_ptr[-1] == info["nnz"] == len(col_idx)
+            # every listed block is inside the mask, keys ascending per row
+            for qb in range(info["n_qblocks"]):
+                kbs = col_idx[row_ptr[qb]:row_ptr[qb + 1]]
+                assert np.all(np.diff(kbs) > 0)
+                f = qb * bq // t
+                vis = brute_visible(f, frames, w, r)
+                assert all((kb * bk) // t in vis for kb in kbs)
+    pairs = {(5, 1, 0): 16, (21, 1, 0): 80, (13, 2, 0): 69, (14, 13, 0): 196}
+    for (frames, w, r), want in pairs.items():
+        assert sum(len(brute_visible(f, frames, w, r)) for f in range(frames)) == want
+        assert orc.active_pairs(frames, 16, w, r) == want * 256
+
+
+def check_plan_negative_control(orc):
+    """128-token blocks on 1200-token frames straddle frame edges: partial blocks."""
+    cls = orc.block_classes(21, 1200, 1, 0, 128, 128)
+    assert (cls == 2).sum() > 0
+    cls = orc.block_classes(21, 1200, 1, 0, 240, 80)
+    assert (cls == 2).sum() == 0
+
+
+def check_invariances(orc):
+    frames, t, d, w, r = 4, 16, 8, 1, 0
+    n = frames * t
+    q, k, v = (_rand((1, 3, n, d), 70 + s) for s in range(3))
+    scale = 0.35
+    base = orc.attention(q, k, v, frames, t, w, r, scale)
+    # permuting keys (with their values) inside each frame leaves o unchanged
+    perm = np.concatenate([f * t + np.random.default_rng(f).permutation(t) for f in range(frames)])
+    o = orc.attention(q, k[:, :, perm], v[:, :, perm], frames, t, w, r, scale)
+    np.testing.assert_allclose(o, base, rtol=0, atol=1e-12)
+    # heads are independent: any head subset computed alone gives the same rows
+    for sel in ([0], [2], [1, 2]):
+        o = orc.attention(q[:, sel], k[:, sel], v[:, sel], frames, t, w, r, scale)
+        np.testing.assert_array_equal(o, base[:, sel])
+    # moving keys across a frame edge changes the result (the mask is not key-symmetric)
+    perm2 = np.arange(n)
+    perm2[[t - 1, t]] = perm2[[t, t - 1]]
+    o = orc.attention(q, k[:, :, perm2], v[:, :, perm2], frames, t, 0, 3, scale)
+    o0 = orc.attention(q, k, v, frames, t, 0, 3, scale)
+    assert np.abs(o - o0).max() > 1e-6
+
+
+ALL_CHECKS = [
+    check_golden_attention, check_golden_plans, check_brute_force, check_weights,
+    check_dense_limit, check_closed_forms, check_bound_shift_exact, check_cauchy_schwarz,
+    check_plan_closed_form, check_plan_negative_control, check_invariances,
+]

@@ -1,0 +1,131 @@
+"""Planted mistakes in the CPU oracle must be caught by its pins.
+
+Each mutant is a copy of the oracle with one plausible mistake (a dropped
+term, a wrong sign or index, a transposed operand, a wrong reduction). The
+test runs the pin checks of ``oracle_pins`` against the mutant and requires at
+least one of them to fail. Mistakes are planted on the CPU, in the oracle only.
+"""
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import fsa_oracle as fo
+from tests import oracle_pins
+
+
+def _namespace(**overrides):
+    ns = types.SimpleNamespace(**{name: getattr(oracle, name) for name in oracle.__all__})
+    for key, val in overrides.items():
+        setattr(ns, key, val)
+    return ns
+
+
+def _vis_no_ref(f, frames, window, ref_frame):
+    return sorted(set(range(max(0, f - window), min(frames - 1, f + window) + 1)))
+
+
+def _vis_wrap(f, frames, window, ref_frame):
+    return sorted({(f + d) % frames for d in range(-window, window + 1)} | {ref_frame})
+
+
+def _vis_short(f, frames, window, ref_frame):
+    return sorted(set(range(max(0, f - window), min(frames - 1, f + window - 1) + 1)) | {ref_frame})
+
+
+def _vis_ref_query_global(f, frames, window, ref_frame):
+    if f == ref_frame:
+        return list(range(frames))
+    return sorted(set(range(max(0, f - window), min(frames - 1, f + window) + 1)) | {ref_frame})
+
+
+def _attention_wrong_axis(q, k, v, frames, t, window, ref_frame, scale):
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    vis = fo.frame_visibility(frames, window, ref_frame)
+    key_frame = np.arange(q.shape[2]) // t
+    out = np.empty_like(q)
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            for f in range(frames):
+                rows = slice(f * t, (f + 1) * t)
+                s = scale * (q[b, h, rows] @ k[b, h].T)
+                s = np.where(vis[f][key_frame][None, :], s, -np.inf)
+                p = np.exp(s - s.max(axis=1, keepdims=True))
+                out[b, h, rows] = (p @ v[b, h]) / p.sum(axis=0).sum()
+    return out
+
+
+def _bounds_kmin(q, k, frames, t, window, ref_frame, scale, block_q=0, block_k=0,
+                 bound_limit=32.0):
+    res = oracle.bounds(q, k, frames, t, window, ref_frame, scale, block_q, block_k, bound_limit)
+    info = res["info"]
+    kn = np.sqrt((np.asarray(k, dtype=np.float64) ** 2).sum(-1))
+    res["kmax"] = kn.reshape(*kn.shape[:2], info["n_kblocks"], info["block_k"]).min(-1)
+    return res
+
+
+def _bounds_global(q, k, frames, t, window, ref_frame, scale, block_q=0, block_k=0,
+                   bound_limit=32.0):
+    res = oracle.bounds(q, k, frames, t, window, ref_frame, scale, block_q, block_k, bound_limit)
+    qn = res["qnorm"]
+    kn = np.sqrt((np.asarray(k, dtype=np.float64) ** 2).sum(-1)).max(-1)
+    res["row_bound"] = scale * qn * kn[..., None]
+    return res
+
+
+def _bounds_no_sqrt(q, k, frames, t, window, ref_frame, scale, block_q=0, block_k=0,
+                    bound_limit=32.0):
+    res = oracle.bounds(q, k, frames, t, window, ref_frame, scale, block_q, block_k, bound_limit)
+    res["row_bound"] = res["row_bound"] * res["qnorm"]
+    return res
+
+
+def _plan_descending(*args, **kw):
+    info, row_ptr, col_idx = oracle.plan(*args, **kw)
+    col = col_idx.copy()
+    for qb in range(info["n_qblocks"]):
+        col[row_ptr[qb]:row_ptr[qb + 1]] = col[row_ptr[qb]:row_ptr[qb + 1]][::-1]
+    return info, row_ptr, col
+
+
+def _plan_swapped_sizes(frames, t, window, ref_frame, block_q=0, block_k=0):
+    return oracle.plan(frames, t, window, ref_frame, block_k, block_q)
+
+
+MUTANTS = {
+    "reference frame dropped": dict(module={"visible_frames": _vis_no_ref}),
+    "window wraps around": dict(module={"visible_frames": _vis_wrap}),
+    "window one frame short": dict(module={"visible_frames": _vis_short}),
+    "reference frame global as query": dict(module={"visible_frames": _vis_ref_query_global}),
+    "scale dropped": dict(ns={"attention": lambda q, k, v, F, T, w, r, s: oracle.attention(
+        q, k, v, F, T, w, r, 1.0)}),
+    "keys used as values": dict(ns={"attention": lambda q, k, v, F, T, w, r, s: oracle.attention(
+        q, k, k, F, T, w, r, s)}),
+    "q and k swapped": dict(ns={"attention": lambda q, k, v, F, T, w, r, s: oracle.attention(
+        k, q, v, F, T, w, r, s)}),
+    "softmax normalised over the wrong axis": dict(ns={"attention": _attention_wrong_axis}),
+    "key-block max taken as min": dict(ns={"bounds": _bounds_kmin}),
+    "row bound over all keys": dict(ns={"bounds": _bounds_global}),
+    "row bound with a squared query norm": dict(ns={"bounds": _bounds_no_sqrt}),
+    "key blocks listed descending": dict(ns={"plan": _plan_descending}),
+    "query and key block sizes swapped": dict(ns={"plan": _plan_swapped_sizes}),
+}
+
+FAST_CHECKS = [c for c in oracle_pins.ALL_CHECKS if c is not oracle_pins.check_plan_closed_form]
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    spec = MUTANTS[name]
+    for attr, fn in spec.get("module", {}).items():
+        monkeypatch.setattr(fo, attr, fn)
+    ns = _namespace(**spec.get("ns", {}))
+    failures = []
+    for check in FAST_CHECKS + [oracle_pins.check_plan_closed_form]:
+        try:
+            check(ns)
+        except Exception as exc:           # noqa: BLE001 - any failure counts
+            failures.append((check.__name__, type(exc).__name__))
+            break
+    assert failures, f"no pin caught the planted mistake: {name}"
