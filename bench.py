@@ -1,0 +1,205 @@
+"""Benchmark of the frame-windowed sparse attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload sr720] [--no-cpu-baseline]
+
+One step is one pass of every stage of the path over one batch of synthetic
+input already resident in HBM: the host plan (fsa_plan into pinned memory and
+an async copy of its CSR to the device), fsa_bounds (norm array and per-head
+eligibility) and fsa_attention. W untimed steps, then K timed steps between two
+device synchronisations. Prints ONE JSON line:
+
+* value = active-block FLOPs (4 D per visible query/key pair) x K / time of the
+  K steps, in TFLOP/s, and pct_of_peak against the bf16 dense MFMA peak;
+* roofline: fsa_attention (the dominant kernel, MFMA-bound) with its mean
+  duration from HIP events recorded on its launch stream around each launch;
+* cpu_baseline: the fp64 oracle (not tuned) timed on one head of the same
+  workload on the host cores, scaled to the same unit.
+
+Only one GPU is used: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOP/s on active blocks + % of bf16 MFMA peak, 25k-token SR attn"
+PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="sr720")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=1,
+                    help="heads of the workload the CPU oracle is timed on")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, qc, kc, vc, heads: int):
+    """Time the fp64 oracle on the first `heads` heads of batch item 0."""
+    import numpy as np
+
+    import oracle
+    import synthetic
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:                                  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    sl = slice(0, heads)
+    q, k, v = (synthetic.to_f64(x[:1, sl]) for x in (qc, kc, vc))
+    t0 = time.perf_counter()
+    o = oracle.attention(q, k, v, wl.frames, wl.tokens_per_frame, wl.window, wl.ref_frame, wl.scale)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(o).all()
+    flops = oracle.active_flops(1, heads, wl.head_dim, wl.frames, wl.tokens_per_frame,
+                                wl.window, wl.ref_frame)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"batch 0, heads 0..{heads - 1} of {wl.heads}, all {wl.frames} frames "
+                      f"({flops:.3e} active FLOPs; dense fp64 masked softmax), {dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
+              "head across GPUs but no multi-GPU run is built.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import frame_windowed_block_amd as fsa
+    import synthetic
+
+    wl = synthetic.WORKLOADS[args.workload]
+    qc, kc, vc = synthetic.make_inputs(wl)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (x.to(dev) for x in (qc, kc, vc))
+    o = torch.empty_like(q)
+
+    # plan: computed on the host every step into pinned memory, copied async
+    info0, rp0, ci0 = fsa.plan(wl.frames, wl.tokens_per_frame, wl.window, wl.ref_frame)
+    dplan = fsa.DevicePlan(wl.frames, wl.tokens_per_frame, wl.window, wl.ref_frame, device=dev)
+    pinned = [(torch.empty(rp0.size, dtype=torch.int32).pin_memory(),
+               torch.empty(ci0.size, dtype=torch.int32).pin_memory()) for _ in range(2)]
+    copied = [None, None]
+    import ctypes
+    L = fsa.lib()
+    P32 = ctypes.POINTER(ctypes.c_int32)
+    bsz, heads, n, d = q.shape
+    qn = torch.empty((bsz, heads, n), dtype=torch.float32, device=dev)
+    km = torch.empty((bsz, heads, info0.n_kblocks), dtype=torch.float32, device=dev)
+    el = torch.empty((bsz, heads), dtype=torch.int32, device=dev)
+    bm = torch.empty((bsz, heads), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        slot = i & 1
+        if copied[slot] is not None:
+            copied[slot].synchronize()                  # pinned buffer free again
+        rp, ci = pinned[slot]
+        info = fsa.PlanInfo()
+        st = L.fsa_plan(wl.frames, wl.tokens_per_frame, wl.window, wl.ref_frame, 0, 0,
+                        ctypes.byref(info), ctypes.cast(rp.data_ptr(), P32), rp.numel(),
+                        ctypes.cast(ci.data_ptr(), P32), ci.numel())
+        assert st == 0
+        dplan.row_ptr.copy_(rp, non_blocking=True)
+        dplan.col_idx.copy_(ci, non_blocking=True)
+        e = torch.cuda.Event()
+        e.record(stream)
+        copied[slot] = e
+        if ev is not None:
+            ev[0].record(stream)
+        fsa.bounds(dplan, q, k, wl.scale, 0.0, 0, 0, qn, km, el, bm, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fsa.attention(dplan, q, k, v, qn, km, el, wl.scale, 0, 0, out=o, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    attn_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    bnd_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+
+    import oracle
+    flops = oracle.active_flops(wl.batch, wl.heads, wl.head_dim, wl.frames, wl.tokens_per_frame,
+                                wl.window, wl.ref_frame)
+    ms_per_step = total_ms / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    attn_mean = float(attn_ms.mean())
+    achieved = flops / (attn_mean * 1e-3) / 1e12
+    bounds_bytes = 2 * bsz * heads * n * d * 2 + 4 * bsz * heads * (n + info0.n_kblocks + 2)
+    eligible = el.cpu().numpy()
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": wl.batch, "heads": wl.heads, "head_dim": wl.head_dim,
+            "frames": wl.frames, "tokens_per_frame": wl.tokens_per_frame, "seq_len": wl.seq_len,
+            "window": wl.window, "ref_frame": wl.ref_frame, "block_q": info0.block_q,
+            "block_k": info0.block_k, "nnz": info0.nnz, "active_flops": flops,
+            "eligible_heads": int(eligible.sum()),
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "kernel": "fsa_attention",
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "mean_ms": round(attn_mean, 5),
+            "p10_ms": round(float(np.percentile(attn_ms, 10)), 5),
+            "p90_ms": round(float(np.percentile(attn_ms, 90)), 5),
+        },
+        "bounds": {
+            "kernels": "fsa_bounds (norms + bound reduce)",
+            "mean_ms": round(float(bnd_ms.mean()), 5),
+            "gbps": round(bounds_bytes / (float(bnd_ms.mean()) * 1e-3) / 1e9, 1),
+            "peak_gbps": PEAK_HBM_GBPS,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, qc, kc, vc, args.cpu_heads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,141 @@
+// Host side of libfsa: argument checks of the device entry points and the
+// hand-off to the kernel launchers. Plain C++ (no device code, no HIP headers):
+// every check runs before anything is enqueued, so a rejected call launches
+// nothing and leaves every output untouched.
+#include <cmath>
+#include <cstdint>
+
+#include "fsa_internal.h"
+
+namespace fsa {
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shared checks of batch / heads / head range / head_dim / scale. On FSA_OK,
+// *count holds the resolved head count and *empty says whether there is no work.
+fsa_status check_common(const fsa_plan_info *plan, int32_t batch, int32_t heads, int32_t head_dim,
+                        int32_t head_offset, int32_t head_count, float scale, int32_t *count,
+                        bool *empty) {
+    fsa_status s = check_plan_info(plan);
+    if (s != FSA_OK) return s;
+    if (batch < 0) return fail(FSA_ERR_INVALID_ARG, "batch = %d, must be >= 0", batch);
+    if (heads < 0) return fail(FSA_ERR_INVALID_ARG, "heads = %d, must be >= 0", heads);
+    if (head_offset < 0 || head_offset > heads)
+        return fail(FSA_ERR_INVALID_ARG, "head_offset = %d outside [0, %d]", head_offset, heads);
+    if (head_count < 0)
+        return fail(FSA_ERR_INVALID_ARG, "head_count = %d, must be >= 0", head_count);
+    const int32_t hc = head_count == 0 ? heads - head_offset : head_count;
+    if (int64_t(head_offset) + hc > heads)
+        return fail(FSA_ERR_INVALID_ARG, "head range [%d, %lld) exceeds heads = %d", head_offset,
+                    (long long)(int64_t(head_offset) + hc), heads);
+    if (head_dim <= 0) return fail(FSA_ERR_INVALID_ARG, "head_dim = %d, must be > 0", head_dim);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(FSA_ERR_UNSUPPORTED, "head_dim = %d; built for 64 and 128", head_dim);
+    if (!(scale > 0.0f) || !std::isfinite(scale))
+        return fail(FSA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    // element counts in 64-bit; keep every offset well inside int64
+    const int64_t elems = int64_t(batch) * heads * plan->seq_len * head_dim;
+    if (batch > 0 && heads > 0 && elems / batch / heads / plan->seq_len != head_dim)
+        return fail(FSA_ERR_INVALID_ARG, "tensor size overflows");
+    if (elems > (int64_t(1) << 60)) return fail(FSA_ERR_INVALID_ARG, "tensor size overflows");
+    *count = hc;
+    *empty = batch == 0 || hc == 0;
+    return FSA_OK;
+}
+
+fsa_status check_csr(const int32_t *row_ptr, const int32_t *col_idx) {
+    if (!row_ptr || !col_idx) return fail(FSA_ERR_INVALID_ARG, "device plan arrays must be non-NULL");
+    if (!aligned(row_ptr, 4) || !aligned(col_idx, 4))
+        return fail(FSA_ERR_INVALID_ARG, "device plan arrays must be 4-byte aligned");
+    return FSA_OK;
+}
+
+fsa_status check_bf16(const void *p, const char *name) {
+    if (!p) return fail(FSA_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!aligned(p, 16)) return fail(FSA_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+    return FSA_OK;
+}
+
+fsa_status check_word(const void *p, const char *name) {
+    if (!p) return fail(FSA_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!aligned(p, 4)) return fail(FSA_ERR_INVALID_ARG, "%s must be 4-byte aligned", name);
+    return FSA_OK;
+}
+
+#define FSA_TRY(expr)                       \
+    do {                                    \
+        fsa_status _s = (expr);             \
+        if (_s != FSA_OK) return _s;        \
+    } while (0)
+
+}  // namespace
+}  // namespace fsa
+
+extern "C" {
+
+fsa_status fsa_bounds(const fsa_plan_info *plan, const int32_t *d_row_ptr, const int32_t *d_col_idx,
+                      const void *q, const void *k, int32_t batch, int32_t heads, int32_t head_dim,
+                      int32_t head_offset, int32_t head_count, float scale, float bound_limit,
+                      float *qnorm, float *kmax, int32_t *eligible, float *bmax, void *stream) {
+    using namespace fsa;
+    clear_error();
+    int32_t hc = 0;
+    bool empty = false;
+    FSA_TRY(check_common(plan, batch, heads, head_dim, head_offset, head_count, scale, &hc, &empty));
+    if (empty) return FSA_OK;
+    FSA_TRY(check_csr(d_row_ptr, d_col_idx));
+    FSA_TRY(check_bf16(q, "q"));
+    FSA_TRY(check_bf16(k, "k"));
+    FSA_TRY(check_word(qnorm, "qnorm"));
+    FSA_TRY(check_word(kmax, "kmax"));
+    FSA_TRY(check_word(eligible, "eligible"));
+    FSA_TRY(check_word(bmax, "bmax"));
+    const int64_t units = int64_t(batch) * hc * (plan->seq_len / 16 + plan->n_kblocks);
+    if (units / 4 + 1 > kMaxWorkgroups || int64_t(batch) * hc * plan->n_qblocks > kMaxWorkgroups)
+        return fail(FSA_ERR_UNSUPPORTED, "problem needs more workgroups than one launch holds");
+    if (!(bound_limit > 0.0f)) bound_limit = 32.0f;               // <= 0 or NaN: default
+    BoundsLaunch a{plan, d_row_ptr, d_col_idx, q, k, batch, heads, head_dim, head_offset, hc,
+                   scale, bound_limit, qnorm, kmax, eligible, bmax, stream};
+    const int err = launch_bounds(a);
+    if (err) return fail(FSA_ERR_HIP, "fsa_bounds launch failed: %s", hip_error_text(err));
+    return FSA_OK;
+}
+
+fsa_status fsa_attention(const fsa_plan_info *plan, const int32_t *d_row_ptr, const int32_t *d_col_idx,
+                         const void *q, const void *k, const void *v, void *o,
+                         const float *qnorm, const float *kmax, const int32_t *eligible,
+                         int32_t batch, int32_t heads, int32_t head_dim, float scale,
+                         int32_t head_offset, int32_t head_count, void *stream) {
+    using namespace fsa;
+    clear_error();
+    int32_t hc = 0;
+    bool empty = false;
+    FSA_TRY(check_common(plan, batch, heads, head_dim, head_offset, head_count, scale, &hc, &empty));
+    if (empty) return FSA_OK;
+    FSA_TRY(check_csr(d_row_ptr, d_col_idx));
+    FSA_TRY(check_bf16(q, "q"));
+    FSA_TRY(check_bf16(k, "k"));
+    FSA_TRY(check_bf16(v, "v"));
+    FSA_TRY(check_bf16(o, "o"));
+    FSA_TRY(check_word(qnorm, "qnorm"));
+    FSA_TRY(check_word(kmax, "kmax"));
+    FSA_TRY(check_word(eligible, "eligible"));
+    // o must not overlap an input: the kernel reads q, k, v while writing o
+    const int64_t bytes = int64_t(batch) * heads * plan->seq_len * head_dim * 2;
+    const uintptr_t ob = reinterpret_cast<uintptr_t>(o);
+    for (const void *in : {q, k, v}) {
+        const uintptr_t ib = reinterpret_cast<uintptr_t>(in);
+        if (ob < ib + uintptr_t(bytes) && ib < ob + uintptr_t(bytes))
+            return fail(FSA_ERR_INVALID_ARG, "o overlaps an input");
+    }
+    if (int64_t(batch) * hc * plan->n_qblocks + 8 > kMaxWorkgroups)
+        return fail(FSA_ERR_UNSUPPORTED, "problem needs more workgroups than one launch holds");
+    AttentionLaunch a{plan, d_row_ptr, d_col_idx, q, k, v, o, qnorm, kmax, eligible,
+                      batch, heads, head_dim, head_offset, hc, scale, stream};
+    const int err = launch_attention(a);
+    if (err) return fail(FSA_ERR_HIP, "fsa_attention launch failed: %s", hip_error_text(err));
+    return FSA_OK;
+}
+
+}  // extern "C"

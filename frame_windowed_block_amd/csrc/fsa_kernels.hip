@@ -1,0 +1,629 @@
+// HIP kernels of libfsa for AMD Instinct MI355X (gfx950, CDNA4).
+//
+// Sources: the pages on the HeyGen / Google Cloud Avatar IV port
+//   [vi:Mask]    aihot.vn, "HeyGen tối ưu hóa mô hình Avatar IV trên Google Cloud
+//                Trillium TPU", section "Xóa bỏ mặt nạ (Mask)" and Fig. 3;
+//   [vi:Softmax] same page, section "Giải phóng Softmax" and Fig. 4;
+//   [uk:Softmax] bib.com.ua, "HeyGen прискорила Avatar IV на TPU у 1,86 раза",
+//                section on breaking the softmax serial chain.
+//
+// fsa_bounds runs two kernels. norms_kernel streams q and k once (the HBM-bound
+// part): it writes ||q_i|| per row and, per key block, the largest ||k_j||
+// ("a small array of precomputed norms", [vi:Softmax]). bound_reduce_kernel
+// then derives, per query block, scale * max ||q_i|| * max kmax over the
+// block's active key blocks, folds it into the head's largest row bound, and
+// the last block of each head writes the head's eligibility ([vi:Softmax]:
+// eligibility is checked per attention head).
+//
+// fsa_attention is one kernel: one workgroup per (batch, head, query block).
+// It walks the query block's active key-block list once, window and reference
+// frame alike ([vi:Mask]: one pass covers the whole mask), in 32-key chunks
+// that may join the 16-key tail of one block to the head of the next; no chunk
+// needs a mask predicate, and an odd count of 16-key tiles leaves one half
+// chunk at the very end. Per chunk:
+//   S^T = K Q^T       bf16 MFMA 16x16x32 (K rows permuted so that each lane
+//                     ends up holding 8 consecutive keys of one query row)
+//   P   = exp2(S * scale * log2e - B_i * log2e)
+//                     B_i = scale * ||q_i|| * max kmax over the row's active
+//                     key blocks, fixed before the loop ([vi:Softmax]); no
+//                     running max, no rescale
+//   O^T += V^T P^T    bf16 MFMA 16x16x32 with V staged transposed in LDS
+// Heads whose bound is too loose run the same walk with the standard running
+// max and rescale instead ([vi:Softmax], Fig. 4), chosen by a branch that is
+// uniform over the workgroup.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fsa_internal.h"
+
+namespace fsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+__device__ __forceinline__ float sumsq8(u32x4 x) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float a = bf16_lo(x[i]), b = bf16_hi(x[i]);
+        s = fmaf(a, a, s);
+        s = fmaf(b, b, s);
+    }
+    return s;
+}
+
+// Max that lets a NaN through (a NaN norm must make the head ineligible).
+__device__ __forceinline__ float nan_max(float a, float b) { return (b > a || b != b) ? b : a; }
+
+// --------------------------------------------------------------------------
+// fsa_bounds, kernel 1: row norms of q, largest key norm per key block.
+// Work unit = one wavefront: either QG 16-row groups of q, or one key block.
+// --------------------------------------------------------------------------
+struct NormsParams {
+    const uint16_t *q, *k;
+    float *qnorm, *kmax;
+    int32_t *eligible;
+    float *bmax;
+    int64_t q_units, total_units;
+    int32_t batch, heads, seq_len, h0, hc, block_k, n_kb;
+};
+
+template <int D, int QG>
+__global__ __launch_bounds__(256) void norms_kernel(NormsParams p) {
+    constexpr int LPR = D / 8;          // lanes per row: 16 bytes each
+    constexpr int RPL = 64 / LPR;       // rows covered by one wave-wide load
+    constexpr int LOADS = 16 / RPL;     // loads per 16-row group
+    const int lane = threadIdx.x & 63;
+    const int sub = lane / LPR;
+    const int seg = lane % LPR;
+
+    if (blockIdx.x == 0) {              // accumulators of bound_reduce_kernel
+        const int64_t nbh = int64_t(p.batch) * p.hc;
+        for (int64_t x = threadIdx.x; x < nbh; x += blockDim.x) {
+            const int64_t hb = (x / p.hc) * p.heads + p.h0 + x % p.hc;
+            p.eligible[hb] = 0;
+            p.bmax[hb] = 0.0f;
+        }
+    }
+    const int64_t unit = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (unit >= p.total_units) return;
+
+    if (unit < p.q_units) {
+        const int64_t units_per_head = (p.seq_len / 16 + QG - 1) / QG;
+        const int64_t bh = unit / units_per_head;
+        const int64_t g0 = (unit % units_per_head) * QG;
+        const int64_t hb = (bh / p.hc) * p.heads + p.h0 + bh % p.hc;
+        const uint16_t *base = p.q + hb * p.seq_len * D;
+        float ss[QG][LOADS];
+        u32x4 x[QG][LOADS];
+#pragma unroll
+        for (int gi = 0; gi < QG; ++gi)
+#pragma unroll
+            for (int l = 0; l < LOADS; ++l) {
+                int64_t row = (g0 + gi) * 16 + l * RPL + sub;
+                if (row >= p.seq_len) row = p.seq_len - 1;     // past the head: recompute, not stored
+                x[gi][l] = *reinterpret_cast<const u32x4 *>(base + row * D + seg * 8);
+            }
+#pragma unroll
+        for (int gi = 0; gi < QG; ++gi)
+#pragma unroll
+            for (int l = 0; l < LOADS; ++l) {
+                float s = sumsq8(x[gi][l]);
+#pragma unroll
+                for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+                ss[gi][l] = s;
+            }
+#pragma unroll
+        for (int gi = 0; gi < QG; ++gi)
+#pragma unroll
+            for (int l = 0; l < LOADS; ++l) {
+                const int64_t row = (g0 + gi) * 16 + l * RPL + sub;
+                if (seg == 0 && row < p.seq_len) p.qnorm[hb * p.seq_len + row] = sqrtf(ss[gi][l]);
+            }
+    } else {
+        const int64_t u = unit - p.q_units;
+        const int64_t bh = u / p.n_kb;
+        const int64_t kb = u % p.n_kb;
+        const int64_t hb = (bh / p.hc) * p.heads + p.h0 + bh % p.hc;
+        const uint16_t *base = p.k + (hb * p.seq_len + kb * p.block_k) * D;
+        const int groups = p.block_k / 16;
+        float best = 0.0f;     // largest squared row norm seen by this lane's rows
+        int gi = 0;
+        for (; gi + 2 <= groups; gi += 2) {
+            u32x4 x[2][LOADS];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int l = 0; l < LOADS; ++l)
+                    x[j][l] = *reinterpret_cast<const u32x4 *>(
+                        base + int64_t((gi + j) * 16 + l * RPL + sub) * D + seg * 8);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int l = 0; l < LOADS; ++l) {
+                    float s = sumsq8(x[j][l]);
+#pragma unroll
+                    for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+                    best = nan_max(best, s);
+                }
+        }
+        if (gi < groups) {
+            u32x4 x[LOADS];
+#pragma unroll
+            for (int l = 0; l < LOADS; ++l)
+                x[l] = *reinterpret_cast<const u32x4 *>(base + int64_t(gi * 16 + l * RPL + sub) * D + seg * 8);
+#pragma unroll
+            for (int l = 0; l < LOADS; ++l) {
+                float s = sumsq8(x[l]);
+#pragma unroll
+                for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+                best = nan_max(best, s);
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) best = nan_max(best, __shfl_xor(best, off));
+        if (lane == 0) p.kmax[hb * p.n_kb + kb] = sqrtf(best);
+    }
+}
+
+// --------------------------------------------------------------------------
+// fsa_bounds, kernel 2: per query block, scale * max ||q_i|| * max kmax over
+// its active key blocks; head maximum by an order-independent atomic max;
+// the last query block of a head to finish writes the head's eligibility.
+// --------------------------------------------------------------------------
+struct ReduceParams {
+    const float *qnorm, *kmax;
+    const int32_t *row_ptr, *col_idx;
+    int32_t *eligible;
+    float *bmax;
+    int32_t heads, seq_len, h0, hc, block_q, n_qb, n_kb;
+    float scale, limit;
+};
+
+__global__ __launch_bounds__(64) void bound_reduce_kernel(ReduceParams p) {
+    const int lane = threadIdx.x;
+    const int64_t wg = blockIdx.x;
+    const int64_t bh = wg / p.n_qb;
+    const int32_t qb = int32_t(wg % p.n_qb);
+    const int64_t hb = (bh / p.hc) * p.heads + p.h0 + bh % p.hc;
+    const float *qn = p.qnorm + hb * p.seq_len + int64_t(qb) * p.block_q;
+    float qm = 0.0f;
+    for (int i = lane; i < p.block_q; i += 64) qm = nan_max(qm, qn[i]);
+    const int32_t e0 = p.row_ptr[qb], e1 = p.row_ptr[qb + 1];
+    float km = 0.0f;
+    for (int32_t e = e0 + lane; e < e1; e += 64) km = nan_max(km, p.kmax[hb * p.n_kb + p.col_idx[e]]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        qm = nan_max(qm, __shfl_xor(qm, off));
+        km = nan_max(km, __shfl_xor(km, off));
+    }
+    if (lane == 0) {
+        float bound = p.scale * qm * km;
+        if (bound != bound) bound = __uint_as_float(0x7fc00000u);   // canonical NaN sorts above +inf
+        atomicMax(reinterpret_cast<unsigned int *>(p.bmax + hb), __float_as_uint(bound));
+        __threadfence();
+        const int old = atomicAdd(p.eligible + hb, 1);
+        if (old == p.n_qb - 1) {
+            __threadfence();
+            const float m = __uint_as_float(atomicOr(reinterpret_cast<unsigned int *>(p.bmax + hb), 0u));
+            p.eligible[hb] = (m <= p.limit) ? 1 : 0;
+        }
+    }
+}
+
+// --------------------------------------------------------------------------
+// fsa_attention
+// --------------------------------------------------------------------------
+struct AttnParams {
+    const uint16_t *q, *k, *v;
+    uint16_t *o;
+    const float *qnorm, *kmax;
+    const int32_t *eligible, *row_ptr, *col_idx;
+    int64_t total_wg, per_xcd;
+    int32_t heads, seq_len, h0, hc;
+    int32_t frames, tokens_per_frame, block_q, block_k, n_qb, n_kb;
+    float c;            // scale * log2(e)
+};
+
+constexpr int KC = 32;  // keys per chunk = K of one p.v MFMA step
+
+template <int D>
+struct Geo {
+    static constexpr int SEGS = D / 8;             // 16-byte segments per K row
+    static constexpr int DS = D / 32;              // q.k MFMA steps over d
+    static constexpr int DT = D / 16;              // 16-wide output column tiles
+    static constexpr int K_BYTES = KC * D * 2;     // K chunk [32][D], swizzled segments
+    static constexpr int V_BYTES = KC * D * 2;     // V^T chunk [4 key octets][D][8 keys]
+    static constexpr int STAGE = K_BYTES + V_BYTES;
+};
+
+// Swizzle of K's 16-byte segments: row r stores segment s at s ^ kswz(r). With
+// the permuted row order used by the q.k fragments, the 16 lanes of a quarter
+// wave read 16 different segments of their rows: no LDS bank conflicts.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+    if constexpr (D == 128) return (r & 3) | (((r >> 3) & 3) << 2);
+    else return (r & 3) | (((r >> 3) & 1) << 2);
+}
+
+// Query-block order inside a head: frames from the middle outwards, so the
+// first workgroups of a head share their key window in L2 and the cheaper edge
+// frames (fewer visible frames) run last.
+__device__ __forceinline__ int32_t rank_to_qblock(int32_t rank, int32_t frames, int32_t qpf) {
+    const int32_t fr = rank / qpf, qi = rank % qpf;
+    const int32_t mid = (frames - 1) / 2;
+    const int32_t f = (fr & 1) ? mid + (fr + 1) / 2 : mid - fr / 2;
+    return f * qpf + qi;
+}
+
+template <int D, int RG, int NW>
+struct AttnKernel {
+    using G = Geo<D>;
+    static constexpr int THREADS = 64 * NW;
+
+    // Global -> register staging of one chunk (two 16-key halves).
+    struct Stage {
+        u32x4 k[(KC * G::SEGS + THREADS - 1) / THREADS];
+        uint32_t v[8];
+    };
+
+    static __device__ __forceinline__ void load_chunk(const AttnParams &p, const uint16_t *kh,
+                                                      const uint16_t *vh, int src0, int src1,
+                                                      Stage &st) {
+        const int t = threadIdx.x;
+        constexpr int KL = (KC * G::SEGS + THREADS - 1) / THREADS;
+#pragma unroll
+        for (int x = 0; x < KL; ++x) {
+            const int idx = t + x * THREADS;
+            const int key = idx / G::SEGS, seg = idx % G::SEGS;
+            const int src = key < 16 ? src0 + key : src1 + key - 16;
+            if (key < KC && (key < 16 || src1 >= 0))
+                st.k[x] = *reinterpret_cast<const u32x4 *>(kh + int64_t(src) * D + seg * 8);
+            else
+                st.k[x] = u32x4{0u, 0u, 0u, 0u};
+        }
+        // V: task = (key octet kg, column pair dp); 8 rows x 4 bytes
+        const int kg = t / (D / 2), dp = t % (D / 2);
+        const int base = kg < 2 ? src0 : src1;
+        if (kg < 4 && (kg < 2 || src1 >= 0)) {
+            const uint16_t *vp = vh + int64_t(base + 8 * (kg & 1)) * D + 2 * dp;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) st.v[i] = *reinterpret_cast<const uint32_t *>(vp + int64_t(i) * D);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) st.v[i] = 0u;
+        }
+    }
+
+    static __device__ __forceinline__ void store_chunk(char *stage, const Stage &st) {
+        const int t = threadIdx.x;
+        constexpr int KL = (KC * G::SEGS + THREADS - 1) / THREADS;
+#pragma unroll
+        for (int x = 0; x < KL; ++x) {
+            const int idx = t + x * THREADS;
+            const int key = idx / G::SEGS, seg = idx % G::SEGS;
+            if (key < KC)
+                *reinterpret_cast<u32x4 *>(stage + (key * G::SEGS + (seg ^ kswz<D>(key))) * 16) = st.k[x];
+        }
+        const int kg = t / (D / 2), dp = t % (D / 2);
+        if (kg < 4) {
+            u32x4 lo, hi;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                lo[j] = __builtin_amdgcn_perm(st.v[2 * j + 1], st.v[2 * j], 0x05040100u);
+                hi[j] = __builtin_amdgcn_perm(st.v[2 * j + 1], st.v[2 * j], 0x07060302u);
+            }
+            char *vt = stage + G::K_BYTES;
+            *reinterpret_cast<u32x4 *>(vt + (kg * D + 2 * dp) * 16) = lo;
+            *reinterpret_cast<u32x4 *>(vt + (kg * D + 2 * dp + 1) * 16) = hi;
+        }
+    }
+
+    // One 32-key chunk for the RG row groups of this wave.
+    template <bool ONLINE, bool TAIL>
+    static __device__ __forceinline__ void compute_chunk(const char *stage, const bf16x8 (&qf)[RG][G::DS],
+                                                         f32x4 (&acc)[RG][G::DT], float (&lsum)[RG],
+                                                         float (&mrow)[RG], const float (&brow)[RG],
+                                                         float c) {
+        const int lane = threadIdx.x & 63;
+        const int m = lane & 15, g = lane >> 4;
+        bf16x8 ka[2][G::DS];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r = 8 * (m >> 2) + 4 * j + (m & 3);
+#pragma unroll
+            for (int ds = 0; ds < G::DS; ++ds) {
+                const int seg = 4 * ds + g;
+                ka[j][ds] = *reinterpret_cast<const bf16x8 *>(stage + (r * G::SEGS + (seg ^ kswz<D>(r))) * 16);
+            }
+        }
+        bf16x8 va[G::DT];
+        const char *vt = stage + G::K_BYTES;
+#pragma unroll
+        for (int dt = 0; dt < G::DT; ++dt)
+            va[dt] = *reinterpret_cast<const bf16x8 *>(vt + (g * D + 16 * dt + m) * 16);
+
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ds = 0; ds < G::DS; ++ds) {
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][ds], qf[rg][ds], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][ds], qf[rg][ds], s1, 0, 0, 0);
+            }
+            // this lane: query row m of the group, keys 8g .. 8g+7 of the chunk
+            float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+            float pr[8];
+            if constexpr (!ONLINE) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(x[i], c, -brow[rg]));
+                if constexpr (TAIL) {
+                    if (g >= 2) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) pr[i] = 0.0f;
+                    }
+                }
+            } else {
+                float t[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) t[i] = x[i] * c;
+                if constexpr (TAIL) {
+                    if (g >= 2) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) t[i] = -__builtin_huge_valf();
+                    }
+                }
+                float cm = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])),
+                                 fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
+                cm = fmaxf(cm, __shfl_xor(cm, 16));
+                cm = fmaxf(cm, __shfl_xor(cm, 32));
+                const float mn = fmaxf(mrow[rg], cm);
+                const float alpha = __builtin_amdgcn_exp2f(mrow[rg] - mn);
+                mrow[rg] = mn;
+                lsum[rg] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < G::DT; ++dt) acc[rg][dt] *= alpha;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(t[i] - mn);
+            }
+            lsum[rg] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+            bf16x8 pk;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pk[i] = static_cast<__bf16>(pr[i]);
+#pragma unroll
+            for (int dt = 0; dt < G::DT; ++dt)
+                acc[rg][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pk, acc[rg][dt], 0, 0, 0);
+        }
+    }
+
+    template <bool ONLINE>
+    static __device__ __forceinline__ void walk(const AttnParams &p, char *smem, const uint16_t *kh,
+                                                const uint16_t *vh, int32_t e0, int32_t nhalf,
+                                                const bf16x8 (&qf)[RG][G::DS], f32x4 (&acc)[RG][G::DT],
+                                                float (&lsum)[RG], float (&mrow)[RG], const float (&brow)[RG]) {
+        const int hpb = p.block_k / 16;
+        const int nch = (nhalf + 1) / 2;
+        auto half_src = [&](int h) -> int {
+            return p.col_idx[e0 + h / hpb] * p.block_k + 16 * (h % hpb);
+        };
+        Stage st;
+        if (nch > 0) {
+            load_chunk(p, kh, vh, half_src(0), 1 < nhalf ? half_src(1) : -1, st);
+            store_chunk(smem, st);
+        }
+        if (nch > 1) load_chunk(p, kh, vh, half_src(2), 3 < nhalf ? half_src(3) : -1, st);
+        __syncthreads();
+        for (int ch = 0; ch < nch - 1; ++ch) {
+            store_chunk(smem + ((ch + 1) & 1) * G::STAGE, st);
+            if (ch + 2 < nch) {
+                const int h = 2 * (ch + 2);
+                load_chunk(p, kh, vh, half_src(h), h + 1 < nhalf ? half_src(h + 1) : -1, st);
+            }
+            compute_chunk<ONLINE, false>(smem + (ch & 1) * G::STAGE, qf, acc, lsum, mrow, brow, p.c);
+            __syncthreads();
+        }
+        if (nch > 0) {
+            const char *last = smem + ((nch - 1) & 1) * G::STAGE;
+            if (nhalf & 1)
+                compute_chunk<ONLINE, true>(last, qf, acc, lsum, mrow, brow, p.c);
+            else
+                compute_chunk<ONLINE, false>(last, qf, acc, lsum, mrow, brow, p.c);
+        }
+    }
+
+    static __device__ void run(const AttnParams &p) {
+        __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE];
+        __shared__ float red[NW];
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int m = lane & 15, g = lane >> 4;
+
+        // XCD-aware order: consecutive workgroup ids go to different XCDs, so
+        // give each XCD a contiguous range of (head, query block) work.
+        const int64_t bid = blockIdx.x;
+        const int64_t L = (bid & 7) * p.per_xcd + (bid >> 3);
+        if (L >= p.total_wg) return;
+        const int64_t bh = L / p.n_qb;
+        const int32_t qpf = p.tokens_per_frame / p.block_q;
+        const int32_t qb = rank_to_qblock(int32_t(L % p.n_qb), p.frames, qpf);
+        const int64_t hb = (bh / p.hc) * p.heads + p.h0 + bh % p.hc;
+        const int64_t head_row0 = hb * p.seq_len;
+        const uint16_t *kh = p.k + head_row0 * D;
+        const uint16_t *vh = p.v + head_row0 * D;
+        const int32_t e0 = p.row_ptr[qb], e1 = p.row_ptr[qb + 1];
+        const int32_t nhalf = (e1 - e0) * (p.block_k / 16);
+        const bool online = p.eligible[hb] == 0;
+
+        // bound path: largest key norm over the row's active key blocks
+        float mk = 0.0f;
+        if (!online) {
+            for (int32_t e = e0 + tid; e < e1; e += THREADS) mk = fmaxf(mk, p.kmax[hb * p.n_kb + p.col_idx[e]]);
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) mk = fmaxf(mk, __shfl_xor(mk, off));
+            if (lane == 0) red[wave] = mk;
+            __syncthreads();
+#pragma unroll
+            for (int w = 0; w < NW; ++w) mk = fmaxf(mk, red[w]);
+        }
+
+        const int groups = p.block_q / 16;
+        for (int sub = 0; sub < groups; sub += NW * RG) {
+            const int my_g0 = sub + wave * RG;
+            int rows[RG];
+            bf16x8 qf[RG][G::DS];
+            f32x4 acc[RG][G::DT];
+            float lsum[RG], mrow[RG], brow[RG];
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+                const int grp = my_g0 + rg < groups ? my_g0 + rg : groups - 1;   // clamp idle groups
+                rows[rg] = qb * p.block_q + grp * 16 + m;
+                const uint16_t *qr = p.q + (head_row0 + rows[rg]) * D;
+#pragma unroll
+                for (int ds = 0; ds < G::DS; ++ds)
+                    qf[rg][ds] = *reinterpret_cast<const bf16x8 *>(qr + 32 * ds + 8 * g);
+#pragma unroll
+                for (int dt = 0; dt < G::DT; ++dt) acc[rg][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                lsum[rg] = 0.0f;
+                mrow[rg] = -__builtin_huge_valf();
+                brow[rg] = online ? 0.0f : p.c * p.qnorm[head_row0 + rows[rg]] * mk;
+            }
+            if (online)
+                walk<true>(p, smem, kh, vh, e0, nhalf, qf, acc, lsum, mrow, brow);
+            else
+                walk<false>(p, smem, kh, vh, e0, nhalf, qf, acc, lsum, mrow, brow);
+
+            // epilogue: one cross-lane reduction of the row sums, normalise, bf16, store
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+                float l = lsum[rg];
+                l += __shfl_xor(l, 16);
+                l += __shfl_xor(l, 32);
+                const float inv = 1.0f / l;
+                if (my_g0 + rg < groups) {
+                    uint16_t *orow = p.o + (head_row0 + rows[rg]) * D;
+#pragma unroll
+                    for (int dt = 0; dt < G::DT; ++dt) {
+                        __bf16 h4[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) h4[i] = static_cast<__bf16>(acc[rg][dt][i] * inv);
+                        uint2 w;
+                        w.x = uint32_t(__builtin_bit_cast(uint16_t, h4[0])) |
+                              (uint32_t(__builtin_bit_cast(uint16_t, h4[1])) << 16);
+                        w.y = uint32_t(__builtin_bit_cast(uint16_t, h4[2])) |
+                              (uint32_t(__builtin_bit_cast(uint16_t, h4[3])) << 16);
+                        *reinterpret_cast<uint2 *>(orow + 16 * dt + 4 * g) = w;
+                    }
+                }
+            }
+            if (sub + NW * RG < groups) __syncthreads();     // LDS reused by the next sub-tile
+        }
+    }
+};
+
+template <int D, int RG, int NW>
+__global__ void __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(1, 1)))
+attention_kernel(AttnParams p) {
+    AttnKernel<D, RG, NW>::run(p);
+}
+
+constexpr int kRG = 4;   // 16-row groups per wavefront (64 query rows)
+constexpr int kNW = 4;   // wavefronts per workgroup (256 query rows)
+
+}  // namespace
+
+const char *hip_error_text(int code) { return hipGetErrorString(static_cast<hipError_t>(code)); }
+
+int launch_bounds(const BoundsLaunch &a) {
+    const fsa_plan_info &pl = *a.plan;
+    hipStream_t stream = static_cast<hipStream_t>(a.stream);
+    constexpr int QG = 2;
+    NormsParams np;
+    np.q = static_cast<const uint16_t *>(a.q);
+    np.k = static_cast<const uint16_t *>(a.k);
+    np.qnorm = a.qnorm;
+    np.kmax = a.kmax;
+    np.eligible = a.eligible;
+    np.bmax = a.bmax;
+    const int64_t nbh = int64_t(a.batch) * a.head_count;
+    np.q_units = nbh * ((pl.seq_len / 16 + QG - 1) / QG);
+    np.total_units = np.q_units + nbh * pl.n_kblocks;
+    np.batch = a.batch;
+    np.heads = a.heads;
+    np.seq_len = pl.seq_len;
+    np.h0 = a.head_offset;
+    np.hc = a.head_count;
+    np.block_k = pl.block_k;
+    np.n_kb = pl.n_kblocks;
+    const unsigned grid1 = unsigned((np.total_units + 3) / 4);
+    if (a.head_dim == 128)
+        hipLaunchKernelGGL((norms_kernel<128, QG>), dim3(grid1), dim3(256), 0, stream, np);
+    else
+        hipLaunchKernelGGL((norms_kernel<64, QG>), dim3(grid1), dim3(256), 0, stream, np);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return int(err);
+
+    ReduceParams rp;
+    rp.qnorm = a.qnorm;
+    rp.kmax = a.kmax;
+    rp.row_ptr = a.row_ptr;
+    rp.col_idx = a.col_idx;
+    rp.eligible = a.eligible;
+    rp.bmax = a.bmax;
+    rp.heads = a.heads;
+    rp.seq_len = pl.seq_len;
+    rp.h0 = a.head_offset;
+    rp.hc = a.head_count;
+    rp.block_q = pl.block_q;
+    rp.n_qb = pl.n_qblocks;
+    rp.n_kb = pl.n_kblocks;
+    rp.scale = a.scale;
+    rp.limit = a.bound_limit;
+    const unsigned grid2 = unsigned(nbh * pl.n_qblocks);
+    hipLaunchKernelGGL(bound_reduce_kernel, dim3(grid2), dim3(64), 0, stream, rp);
+    err = hipGetLastError();
+    return err == hipSuccess ? 0 : int(err);
+}
+
+int launch_attention(const AttentionLaunch &a) {
+    const fsa_plan_info &pl = *a.plan;
+    AttnParams p;
+    p.q = static_cast<const uint16_t *>(a.q);
+    p.k = static_cast<const uint16_t *>(a.k);
+    p.v = static_cast<const uint16_t *>(a.v);
+    p.o = static_cast<uint16_t *>(a.o);
+    p.qnorm = a.qnorm;
+    p.kmax = a.kmax;
+    p.eligible = a.eligible;
+    p.row_ptr = a.row_ptr;
+    p.col_idx = a.col_idx;
+    p.total_wg = int64_t(a.batch) * a.head_count * pl.n_qblocks;
+    p.per_xcd = (p.total_wg + 7) / 8;
+    p.heads = a.heads;
+    p.seq_len = pl.seq_len;
+    p.h0 = a.head_offset;
+    p.hc = a.head_count;
+    p.frames = pl.frames;
+    p.tokens_per_frame = pl.tokens_per_frame;
+    p.block_q = pl.block_q;
+    p.block_k = pl.block_k;
+    p.n_qb = pl.n_qblocks;
+    p.n_kb = pl.n_kblocks;
+    p.c = a.scale * kLog2e;
+    const unsigned grid = unsigned(p.per_xcd * 8);
+    hipStream_t stream = static_cast<hipStream_t>(a.stream);
+    if (a.head_dim == 128)
+        hipLaunchKernelGGL((attention_kernel<128, kRG, kNW>), dim3(grid), dim3(64 * kNW), 0, stream, p);
+    else
+        hipLaunchKernelGGL((attention_kernel<64, kRG, kNW>), dim3(grid), dim3(64 * kNW), 0, stream, p);
+    const hipError_t err = hipGetLastError();
+    return err == hipSuccess ? 0 : int(err);
+}
+
+}  // namespace fsa

@@ -1,0 +1,143 @@
+"""The C-ABI library on the CPU: it loads, exports what include/fsa.h
+declares, and rejects invalid arguments on the host before any launch."""
+import ctypes
+
+import pytest
+
+import frame_windowed_block_amd as fsa
+from frame_windowed_block_amd import _abi
+
+
+def test_exports_every_declared_symbol():
+    L = fsa.lib()
+    names = fsa.header_symbols()
+    assert {"fsa_plan", "fsa_bounds", "fsa_attention", "fsa_status_string",
+            "fsa_last_error", "fsa_version"} <= set(names)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_version_and_strings():
+    assert fsa.version() == 10000
+    L = fsa.lib()
+    for code in range(6):
+        assert L.fsa_status_string(code)
+    assert L.fsa_status_string(99) == b"unknown status"
+
+
+def _plan_info(frames=5, t=80, w=1, r=0):
+    info, _, _ = fsa.plan(frames, t, w, r)
+    return info
+
+
+FAKE = 0x10000          # a 64 KiB-aligned address that is never dereferenced
+
+
+def _bounds(info, **kw):
+    args = dict(row_ptr=FAKE, col_idx=FAKE, q=FAKE, k=FAKE, batch=1, heads=2, head_dim=64,
+                head_offset=0, head_count=0, scale=0.125, bound_limit=0.0, qnorm=FAKE,
+                kmax=FAKE, eligible=FAKE, bmax=FAKE)
+    args.update(kw)
+    L = fsa.lib()
+    st = L.fsa_bounds(ctypes.byref(info) if info is not None else None,
+                      args["row_ptr"], args["col_idx"], args["q"], args["k"], args["batch"],
+                      args["heads"], args["head_dim"], args["head_offset"], args["head_count"],
+                      args["scale"], args["bound_limit"], args["qnorm"], args["kmax"],
+                      args["eligible"], args["bmax"], None)
+    return st, L.fsa_last_error().decode()
+
+
+def _attn(info, **kw):
+    args = dict(row_ptr=FAKE, col_idx=FAKE, q=FAKE, k=FAKE * 4096, v=FAKE * 8192, o=FAKE * 16384,
+                qnorm=FAKE, kmax=FAKE, eligible=FAKE, batch=1, heads=2, head_dim=64, scale=0.125,
+                head_offset=0, head_count=0)
+    args.update(kw)
+    L = fsa.lib()
+    st = L.fsa_attention(ctypes.byref(info) if info is not None else None,
+                         args["row_ptr"], args["col_idx"], args["q"], args["k"], args["v"],
+                         args["o"], args["qnorm"], args["kmax"], args["eligible"], args["batch"],
+                         args["heads"], args["head_dim"], args["scale"], args["head_offset"],
+                         args["head_count"], None)
+    return st, L.fsa_last_error().decode()
+
+
+BAD_COMMON = [
+    (dict(batch=-1), fsa.FSA_ERR_INVALID_ARG),
+    (dict(heads=-2), fsa.FSA_ERR_INVALID_ARG),
+    (dict(head_offset=3), fsa.FSA_ERR_INVALID_ARG),
+    (dict(head_offset=-1), fsa.FSA_ERR_INVALID_ARG),
+    (dict(head_count=-1), fsa.FSA_ERR_INVALID_ARG),
+    (dict(head_offset=1, head_count=2), fsa.FSA_ERR_INVALID_ARG),
+    (dict(head_dim=96), fsa.FSA_ERR_UNSUPPORTED),
+    (dict(head_dim=0), fsa.FSA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fsa.FSA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), fsa.FSA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fsa.FSA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fsa.FSA_ERR_INVALID_ARG),
+    (dict(q=0), fsa.FSA_ERR_INVALID_ARG),
+    (dict(q=FAKE + 8), fsa.FSA_ERR_INVALID_ARG),
+    (dict(k=FAKE + 2), fsa.FSA_ERR_INVALID_ARG),
+    (dict(row_ptr=0), fsa.FSA_ERR_INVALID_ARG),
+    (dict(col_idx=FAKE + 2), fsa.FSA_ERR_INVALID_ARG),
+    (dict(qnorm=0), fsa.FSA_ERR_INVALID_ARG),
+    (dict(kmax=FAKE + 1), fsa.FSA_ERR_INVALID_ARG),
+    (dict(eligible=0), fsa.FSA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("kw,want", BAD_COMMON)
+def test_bounds_rejects(kw, want):
+    st, msg = _bounds(_plan_info(), **kw)
+    assert st == want and msg
+
+
+@pytest.mark.parametrize("kw,want", BAD_COMMON + [
+    (dict(v=0), fsa.FSA_ERR_INVALID_ARG),
+    (dict(o=FAKE * 16384 + 4), fsa.FSA_ERR_INVALID_ARG),
+    (dict(o=FAKE), fsa.FSA_ERR_INVALID_ARG),                 # overlaps q
+])
+def test_attention_rejects(kw, want):
+    st, msg = _attn(_plan_info(), **kw)
+    assert st == want and msg
+
+
+@pytest.mark.parametrize("kw", [dict(bmax=0), dict(bmax=FAKE + 2)])
+def test_bounds_requires_bmax(kw):
+    st, _ = _bounds(_plan_info(), **kw)
+    assert st == fsa.FSA_ERR_INVALID_ARG
+
+
+def test_plan_info_must_be_consistent():
+    info = _plan_info()
+    assert _bounds(None)[0] == fsa.FSA_ERR_INVALID_ARG
+    for field, val in (("nnz", 15), ("n_qblocks", 4), ("seq_len", 401), ("block_q", 0),
+                       ("block_k", 48), ("tokens_per_frame", 72), ("ref_frame", 5)):
+        bad = _abi.PlanInfo.from_buffer_copy(info)
+        setattr(bad, field, val)
+        st, msg = _bounds(bad)
+        assert st in (fsa.FSA_ERR_INVALID_ARG, fsa.FSA_ERR_UNALIGNED), field
+        st, msg = _attn(bad)
+        assert st in (fsa.FSA_ERR_INVALID_ARG, fsa.FSA_ERR_UNALIGNED), field
+
+
+def test_empty_work_is_a_noop():
+    # no device work, so null pointers are fine and nothing is launched
+    info = _plan_info()
+    assert _bounds(info, batch=0, q=0, k=0, qnorm=0)[0] == fsa.FSA_OK
+    assert _attn(info, batch=0, q=0, o=0)[0] == fsa.FSA_OK
+    assert _bounds(info, head_offset=2, head_count=0, q=0)[0] == fsa.FSA_OK
+    assert _attn(info, heads=0, q=0)[0] == fsa.FSA_OK
+
+
+def test_error_text_is_per_call():
+    L = fsa.lib()
+    _bounds(_plan_info(), head_dim=96)
+    assert "head_dim" in L.fsa_last_error().decode()
+    fsa.plan(5, 80, 1, 0)
+    assert L.fsa_last_error().decode() == ""
+
+
+def test_binding_raises():
+    with pytest.raises(fsa.FsaError) as ei:
+        fsa.plan(5, 72, 1, 0)
+    assert ei.value.status == fsa.FSA_ERR_UNALIGNED

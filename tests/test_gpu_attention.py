@@ -1,0 +1,209 @@
+"""HIP path against the fp64 oracle, through the C ABI (needs an MI355X).
+
+Bars: block plans bit-exact (CPU tests), bounds within 1e-5 relative, and
+attention outputs (bf16) within max-abs 1e-2 and relative L2 5e-3 of the
+oracle. Small shapes are compared element by element on every output; the
+full-size workloads on seeded samples of rows (the oracle computes those rows
+exactly) plus whole-tensor properties.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 1e-2
+REL_L2 = 5e-3
+BOUND_RTOL = 1e-5
+
+
+def _fsa():
+    import frame_windowed_block_amd as fsa
+    fsa.lib()
+    return fsa
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run(wl, q, k, v, bq=0, bk=0, bound_limit=0.0, head_offset=0, head_count=0, out=None):
+    fsa = _fsa()
+    dplan = fsa.DevicePlan(wl.frames, wl.tokens_per_frame, wl.window, wl.ref_frame, bq, bk)
+    o, b = fsa.forward(dplan, q, k, v, wl.scale, bound_limit, head_offset, head_count, out=out)
+    torch.cuda.synchronize()
+    return o, b, dplan
+
+
+def _oracle_args(wl):
+    return (wl.frames, wl.tokens_per_frame, wl.window, wl.ref_frame, wl.scale)
+
+
+def _assert_close(got, ref, what):
+    m, r = oracle.max_abs_and_rel_l2(got, ref)
+    _say(f"{what}: max_abs={m:.3e} rel_l2={r:.3e}")
+    assert np.isfinite(got).all(), what
+    assert m <= MAX_ABS, (what, m)
+    assert r <= REL_L2, (what, r)
+
+
+def _check_bounds(wl, qc, kc, b, dplan, bq, bk, bound_limit=0.0):
+    qnorm, kmax, eligible, bmax = (t.cpu().numpy() for t in b)
+    ref = oracle.bounds(synthetic.to_f64(qc), synthetic.to_f64(kc), *_oracle_args(wl),
+                        dplan.info.block_q, dplan.info.block_k, bound_limit)
+    np.testing.assert_allclose(qnorm, ref["qnorm"], rtol=BOUND_RTOL, atol=0)
+    np.testing.assert_allclose(kmax, ref["kmax"], rtol=BOUND_RTOL, atol=0)
+    np.testing.assert_allclose(bmax, ref["bmax"], rtol=BOUND_RTOL, atol=0)
+    limit = oracle.effective_bound_limit(bound_limit)
+    tie = np.abs(ref["bmax"] - limit) <= 1e-4 * limit
+    assert np.all((eligible == ref["eligible"]) | tie)
+    return ref
+
+
+# ----------------------------------------------------------------- small shapes, every output
+SMALL = [
+    # name, B, H, D, F, T, w, r, bq, bk
+    ("tiny", 1, 2, 64, 5, 80, 1, 0, 0, 0),
+    ("t240_w1", 1, 2, 128, 3, 240, 1, 0, 240, 80),
+    ("t48_w0_rlast", 2, 3, 128, 4, 48, 0, 3, 48, 16),
+    ("t16_pair", 1, 1, 128, 2, 16, 0, 0, 16, 16),
+    ("t80_bq16", 1, 2, 64, 5, 80, 2, 4, 16, 80),
+    ("t512_subtiles", 1, 2, 128, 3, 512, 1, 1, 512, 128),
+    ("t1200_small", 1, 1, 128, 3, 1200, 1, 0, 240, 80),
+    ("t144_d64_b2", 2, 2, 64, 4, 144, 1, 2, 144, 48),
+    ("t32_dense", 1, 2, 128, 6, 32, 9, 0, 32, 32),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_parity(case):
+    name, bsz, heads, d, frames, t, w, r, bq, bk = case
+    wl = synthetic.Workload(name, bsz, heads, d, frames, t, w, r, seed=len(name))
+    _say(f"case {name}: B={bsz} H={heads} D={d} F={frames} T={t} w={w} r={r} bq={bq} bk={bk}")
+    qc, kc, vc = synthetic.make_inputs(wl)
+    q, k, v = (x.cuda() for x in (qc, kc, vc))
+    o, b, dplan = _run(wl, q, k, v, bq, bk)
+    _check_bounds(wl, qc, kc, b, dplan, bq, bk)
+    ref = oracle.attention(*(synthetic.to_f64(x) for x in (qc, kc, vc)), *_oracle_args(wl))
+    _assert_close(synthetic.to_f64(o), ref, name)
+    # online fallback forced on every head: same result within tolerance
+    o2, b2, _ = _run(wl, q, k, v, bq, bk, bound_limit=1e-30)
+    assert int(b2[2].sum()) == 0
+    _assert_close(synthetic.to_f64(o2), ref, name + " (online)")
+
+
+# ----------------------------------------------------------------- full-size workloads
+FULL = ["tiny", "sr720", "sr1080", "bound_stress", "dense"]
+_cache = {}
+
+
+def _full(name):
+    if name not in _cache:
+        wl = synthetic.WORKLOADS[name]
+        qc, kc, vc = synthetic.make_inputs(wl)
+        _cache.clear()
+        _cache[name] = (wl, qc, kc, vc)
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_parity(name):
+    wl, qc, kc, vc = _full(name)
+    _say(f"workload {name}: N={wl.seq_len} H={wl.heads} D={wl.head_dim}")
+    q, k, v = (x.cuda() for x in (qc, kc, vc))
+    o, b, dplan = _run(wl, q, k, v)
+    ref_b = _check_bounds(wl, qc, kc, b, dplan, 0, 0)
+    eligible = b[2].cpu().numpy()
+    if name == "bound_stress":
+        assert np.all(eligible == 0)
+    else:
+        assert np.all(eligible == 1)
+    assert torch.isfinite(o).all().item()
+    rows = synthetic.sample_rows(wl, 256 if wl.seq_len > 1000 else 400)
+    ref = oracle.attention_rows(synthetic.to_f64(qc), synthetic.to_f64(kc), synthetic.to_f64(vc),
+                                rows, *_oracle_args(wl))
+    oc = o.cpu()
+    got = np.stack([synthetic.to_f64(oc[bb, hh, ii]) for bb, hh, ii in rows])
+    _assert_close(got, ref, name)
+    del ref_b
+
+
+def test_deterministic_and_grouping_bitwise():
+    """Repeated runs are bitwise equal, and four 2-head calls on four streams
+    equal one 8-head call bitwise (each group sees the ungrouped mask)."""
+    wl, qc, kc, vc = _full("dense")
+    q, k, v = (x.cuda() for x in (qc, kc, vc))
+    fsa = _fsa()
+    o1, b1, dplan = _run(wl, q, k, v)
+    o2, _, _ = _run(wl, q, k, v)
+    assert torch.equal(o1, o2)
+    og = torch.full_like(q, float("nan"))
+    qn, km, el, bm = b1
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    start = torch.cuda.Event()
+    start.record()
+    for gi, s in enumerate(streams):
+        s.wait_event(start)
+        with torch.cuda.stream(s):
+            fsa.attention(dplan, q, k, v, qn, km, el, wl.scale, 2 * gi, 2, out=og, stream=s)
+    torch.cuda.synchronize()
+    assert torch.equal(og, o1)
+    # grouped bounds match ungrouped bounds too
+    b2 = [torch.zeros_like(x) for x in b1]
+    for gi in range(4):
+        fsa.bounds(dplan, q, k, wl.scale, 0.0, 2 * gi, 2, *b2)
+    torch.cuda.synchronize()
+    for x, y in zip(b1, b2):
+        assert torch.equal(x, y)
+
+
+def test_head_range_leaves_other_heads_untouched():
+    wl = synthetic.Workload("hr", 2, 5, 128, 3, 240, 1, 2, seed=3)
+    qc, kc, vc = synthetic.make_inputs(wl)
+    q, k, v = (x.cuda() for x in (qc, kc, vc))
+    fsa = _fsa()
+    dplan = fsa.DevicePlan(wl.frames, wl.tokens_per_frame, wl.window, wl.ref_frame)
+    sentinel = torch.full_like(q, 7.0)
+    qn = torch.full((2, 5, wl.seq_len), -1.0, device="cuda")
+    km = torch.full((2, 5, dplan.info.n_kblocks), -1.0, device="cuda")
+    el = torch.full((2, 5), -3, dtype=torch.int32, device="cuda")
+    bm = torch.full((2, 5), -1.0, device="cuda")
+    fsa.bounds(dplan, q, k, wl.scale, 0.0, 1, 3, qn, km, el, bm)
+    fsa.attention(dplan, q, k, v, qn, km, el, wl.scale, 1, 3, out=sentinel)
+    torch.cuda.synchronize()
+    for h in (0, 4):
+        assert torch.all(sentinel[:, h] == 7.0)
+        assert torch.all(qn[:, h] == -1.0) and torch.all(km[:, h] == -1.0)
+        assert torch.all(el[:, h] == -3) and torch.all(bm[:, h] == -1.0)
+    assert torch.all(el[:, 1:4] == 1)
+    ref = oracle.attention(*(synthetic.to_f64(x[:, 1:4]) for x in (qc, kc, vc)),
+                           *_oracle_args(wl))
+    _assert_close(synthetic.to_f64(sentinel[:, 1:4]), ref, "head range")
+
+
+def test_unsafe_bound_underflows_on_stress_data():
+    """Forcing the bound path on the heavy-tailed workload (limit = +inf)
+    drives whole rows to exp underflow: their sums vanish and the output turns
+    non-finite. This is the hazard the per-head eligibility check guards."""
+    wl, qc, kc, vc = _full("bound_stress")
+    q, k, v = (x.cuda() for x in (qc, kc, vc))
+    o, b, _ = _run(wl, q, k, v, bound_limit=float("inf"))
+    assert int(b[2].sum()) == wl.heads
+    assert not torch.isfinite(o).all().item()
+
+
+def test_empty_batch_is_noop():
+    fsa = _fsa()
+    wl = synthetic.Workload("e", 0, 2, 128, 2, 16, 0, 0)
+    dplan = fsa.DevicePlan(2, 16, 0, 0)
+    q = torch.empty((0, 2, 32, 128), dtype=torch.bfloat16, device="cuda")
+    o, _ = fsa.forward(dplan, q, q.clone(), q.clone(), wl.scale)
+    torch.cuda.synchronize()
+    assert o.shape == q.shape
