@@ -41,7 +41,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="sr720")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=1,
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run torch's device copy of a MIB-sized buffer 5 times (known bytes "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
+    ap.add_argument("--cpu-heads", type=int, default=4,
                     help="heads of the workload the CPU oracle is timed on")
     return ap.parse_args()
 
@@ -82,6 +85,16 @@ def main():
 
     import frame_windowed_block_amd as fsa
     import synthetic
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4}))
+        return
 
     wl = synthetic.WORKLOADS[args.workload]
     qc, kc, vc = synthetic.make_inputs(wl)
