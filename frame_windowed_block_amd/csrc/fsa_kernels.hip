@@ -37,12 +37,27 @@
 
 #include "fsa_internal.h"
 
+// Attention kernel configuration (overridable at build time for tuning sweeps).
+#ifndef FSA_RG
+#define FSA_RG 2      // 16-row query groups per wavefront
+#endif
+#ifndef FSA_NW
+#define FSA_NW 8      // wavefronts per workgroup
+#endif
+#ifndef FSA_KCH
+#define FSA_KCH 64    // keys per LDS stage
+#endif
+#ifndef FSA_WPE
+#define FSA_WPE 2     // wavefronts per SIMD the registers are budgeted for
+#endif
+
 namespace fsa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -176,42 +191,55 @@ __global__ __launch_bounds__(256) void norms_kernel(NormsParams p) {
 
 // --------------------------------------------------------------------------
 // fsa_bounds, kernel 2: per query block, scale * max ||q_i|| * max kmax over
-// its active key blocks; head maximum by an order-independent atomic max;
-// the last query block of a head to finish writes the head's eligibility.
+// its active key blocks. A workgroup covers 16 query blocks (16 lanes each)
+// and folds its maximum into the head's with one order-independent atomic
+// max; the last workgroup of a head to arrive writes the head's eligibility.
 // --------------------------------------------------------------------------
 struct ReduceParams {
     const float *qnorm, *kmax;
     const int32_t *row_ptr, *col_idx;
     int32_t *eligible;
     float *bmax;
-    int32_t heads, seq_len, h0, hc, block_q, n_qb, n_kb;
+    int32_t heads, seq_len, h0, hc, block_q, n_qb, n_kb, chunks;
     float scale, limit;
 };
 
-__global__ __launch_bounds__(64) void bound_reduce_kernel(ReduceParams p) {
-    const int lane = threadIdx.x;
-    const int64_t wg = blockIdx.x;
-    const int64_t bh = wg / p.n_qb;
-    const int32_t qb = int32_t(wg % p.n_qb);
+constexpr int kReduceQB = 16;   // query blocks per workgroup (16 lanes each)
+
+__global__ __launch_bounds__(256) void bound_reduce_kernel(ReduceParams p) {
+    __shared__ float red[4];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int qi = tid / 16, sl = tid % 16;
+    const int64_t bh = blockIdx.x / p.chunks;
+    const int32_t chunk = int32_t(blockIdx.x % p.chunks);
+    const int32_t qb = chunk * kReduceQB + qi;
     const int64_t hb = (bh / p.hc) * p.heads + p.h0 + bh % p.hc;
-    const float *qn = p.qnorm + hb * p.seq_len + int64_t(qb) * p.block_q;
-    float qm = 0.0f;
-    for (int i = lane; i < p.block_q; i += 64) qm = nan_max(qm, qn[i]);
-    const int32_t e0 = p.row_ptr[qb], e1 = p.row_ptr[qb + 1];
-    float km = 0.0f;
-    for (int32_t e = e0 + lane; e < e1; e += 64) km = nan_max(km, p.kmax[hb * p.n_kb + p.col_idx[e]]);
+    float bound = 0.0f;
+    if (qb < p.n_qb) {
+        const float *qn = p.qnorm + hb * p.seq_len + int64_t(qb) * p.block_q;
+        float qm = 0.0f;
+        for (int i = sl; i < p.block_q; i += 16) qm = nan_max(qm, qn[i]);
+        const int32_t e0 = p.row_ptr[qb], e1 = p.row_ptr[qb + 1];
+        float km = 0.0f;
+        for (int32_t e = e0 + sl; e < e1; e += 16) km = nan_max(km, p.kmax[hb * p.n_kb + p.col_idx[e]]);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        qm = nan_max(qm, __shfl_xor(qm, off));
-        km = nan_max(km, __shfl_xor(km, off));
+        for (int off = 8; off >= 1; off >>= 1) {
+            qm = nan_max(qm, __shfl_xor(qm, off));
+            km = nan_max(km, __shfl_xor(km, off));
+        }
+        bound = p.scale * qm * km;
     }
-    if (lane == 0) {
-        float bound = p.scale * qm * km;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) bound = nan_max(bound, __shfl_xor(bound, off));
+    if (lane == 0) red[tid >> 6] = bound;
+    __syncthreads();
+    if (tid == 0) {
+        bound = nan_max(nan_max(red[0], red[1]), nan_max(red[2], red[3]));
         if (bound != bound) bound = __uint_as_float(0x7fc00000u);   // canonical NaN sorts above +inf
         atomicMax(reinterpret_cast<unsigned int *>(p.bmax + hb), __float_as_uint(bound));
         __threadfence();
         const int old = atomicAdd(p.eligible + hb, 1);
-        if (old == p.n_qb - 1) {
+        if (old == p.chunks - 1) {
             __threadfence();
             const float m = __uint_as_float(atomicOr(reinterpret_cast<unsigned int *>(p.bmax + hb), 0u));
             p.eligible[hb] = (m <= p.limit) ? 1 : 0;
@@ -233,16 +261,18 @@ struct AttnParams {
     float c;            // scale * log2(e)
 };
 
-constexpr int KC = 32;  // keys per chunk = K of one p.v MFMA step
-
-template <int D>
+// Geometry of one LDS stage: KCH keys = KCH/32 "sub-steps" of 32 keys, each
+// holding K [32][D] (16-byte segments swizzled) and V^T [4 key octets][D][8].
+template <int D, int KCH>
 struct Geo {
     static constexpr int SEGS = D / 8;             // 16-byte segments per K row
     static constexpr int DS = D / 32;              // q.k MFMA steps over d
     static constexpr int DT = D / 16;              // 16-wide output column tiles
-    static constexpr int K_BYTES = KC * D * 2;     // K chunk [32][D], swizzled segments
-    static constexpr int V_BYTES = KC * D * 2;     // V^T chunk [4 key octets][D][8 keys]
-    static constexpr int STAGE = K_BYTES + V_BYTES;
+    static constexpr int SUB = KCH / 32;           // 32-key p.v MFMA steps per stage
+    static constexpr int QUARTERS = KCH / 16;      // 16-key tiles per stage
+    static constexpr int SUB_K = 32 * D * 2;
+    static constexpr int SUB_BYTES = 2 * SUB_K;    // K then V^T
+    static constexpr int STAGE = SUB * SUB_BYTES;
 };
 
 // Swizzle of K's 16-byte segments: row r stores segment s at s ^ kswz(r). With
@@ -254,6 +284,8 @@ __device__ __forceinline__ int kswz(int r) {
     else return (r & 3) | (((r >> 3) & 1) << 2);
 }
 
+constexpr int ar(int n) { return n > 0 ? n : 1; }   // array extent for n row groups
+
 // Query-block order inside a head: frames from the middle outwards, so the
 // first workgroups of a head share their key window in L2 and the cheaper edge
 // frames (fewer visible frames) run last.
@@ -264,186 +296,318 @@ __device__ __forceinline__ int32_t rank_to_qblock(int32_t rank, int32_t frames, 
     return f * qpf + qi;
 }
 
-template <int D, int RG, int NW>
+// D: head dim. RG: 16-row groups per wavefront. NW: wavefronts per workgroup.
+// KCH: keys per LDS stage (32 or 64).
+template <int D, int RG, int NW, int KCH>
 struct AttnKernel {
-    using G = Geo<D>;
+    using G = Geo<D, KCH>;
     static constexpr int THREADS = 64 * NW;
+    static constexpr int KL = (KCH * G::SEGS + THREADS - 1) / THREADS;            // K segments / thread
+    static constexpr int VTASKS = (KCH / 8) * (D / 2);
+    static constexpr int VL = (VTASKS + THREADS - 1) / THREADS;                   // V tasks / thread
+    static constexpr int LDS_BYTES = 2 * G::STAGE + 64;
 
-    // Global -> register staging of one chunk (two 16-key halves).
+    // Global -> register staging of one stage.
     struct Stage {
-        u32x4 k[(KC * G::SEGS + THREADS - 1) / THREADS];
-        uint32_t v[8];
+        u32x4 k[KL];
+        uint32_t v[VL][8];
     };
 
-    static __device__ __forceinline__ void load_chunk(const AttnParams &p, const uint16_t *kh,
-                                                      const uint16_t *vh, int src0, int src1,
-                                                      Stage &st) {
+    // Source key of each 16-key tile of a stage (-1: past the end of the row).
+    // Named fields, not an array: a lane-varying pick must stay a select chain
+    // rather than become a dynamically indexed (scratch) array.
+    static_assert(G::QUARTERS == 2 || G::QUARTERS == 4, "stages of 32 or 64 keys");
+    struct Src {
+        int q0, q1, q2, q3;
+    };
+    // src[j] for a lane-varying j, computed on values (a select on field
+    // addresses would turn the struct into a dynamically indexed stack array)
+    static __device__ __forceinline__ int pick(int j, int q0, int q1, int q2, int q3) {
+        const int lo = j == 0 ? q0 : q1;
+        const int hi = j == 2 ? q2 : q3;
+        return (G::QUARTERS == 2 || j < 2) ? lo : hi;
+    }
+
+    static __device__ __forceinline__ Src stage_src(const AttnParams &p, int32_t e0, int nquart, int st) {
+        const int hpb = p.block_k / 16;
+        auto one = [&](int j) -> int {
+            const int h = st * G::QUARTERS + j;
+            return h < nquart ? p.col_idx[e0 + h / hpb] * p.block_k + 16 * (h % hpb) : -1;
+        };
+        Src s;
+        s.q0 = one(0);
+        s.q1 = one(1);
+        s.q2 = G::QUARTERS > 2 ? one(2) : -1;
+        s.q3 = G::QUARTERS > 2 ? one(3) : -1;
+        return s;
+    }
+
+    static __device__ __forceinline__ void load_stage(const uint16_t *kh, const uint16_t *vh,
+                                                      const Src src, Stage &st) {
         const int t = threadIdx.x;
-        constexpr int KL = (KC * G::SEGS + THREADS - 1) / THREADS;
+        const int s0 = src.q0, s1 = src.q1, s2 = src.q2, s3 = src.q3;
 #pragma unroll
         for (int x = 0; x < KL; ++x) {
             const int idx = t + x * THREADS;
             const int key = idx / G::SEGS, seg = idx % G::SEGS;
-            const int src = key < 16 ? src0 + key : src1 + key - 16;
-            if (key < KC && (key < 16 || src1 >= 0))
-                st.k[x] = *reinterpret_cast<const u32x4 *>(kh + int64_t(src) * D + seg * 8);
+            const int qs = key < KCH ? pick(key / 16, s0, s1, s2, s3) : -1;
+            if (qs >= 0)
+                st.k[x] = *reinterpret_cast<const u32x4 *>(kh + int64_t(qs + key % 16) * D + seg * 8);
             else
                 st.k[x] = u32x4{0u, 0u, 0u, 0u};
         }
-        // V: task = (key octet kg, column pair dp); 8 rows x 4 bytes
-        const int kg = t / (D / 2), dp = t % (D / 2);
-        const int base = kg < 2 ? src0 : src1;
-        if (kg < 4 && (kg < 2 || src1 >= 0)) {
-            const uint16_t *vp = vh + int64_t(base + 8 * (kg & 1)) * D + 2 * dp;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) st.v[i] = *reinterpret_cast<const uint32_t *>(vp + int64_t(i) * D);
-        } else {
+        for (int x = 0; x < VL; ++x) {
+            const int task = t + x * THREADS;
+            const int oct = task / (D / 2), dp = task % (D / 2);
+            const int qs = oct < KCH / 8 ? pick(oct / 2, s0, s1, s2, s3) : -1;
+            if (qs >= 0) {
+                const uint16_t *vp = vh + int64_t(qs + 8 * (oct & 1)) * D + 2 * dp;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) st.v[i] = 0u;
+                for (int i = 0; i < 8; ++i) st.v[x][i] = *reinterpret_cast<const uint32_t *>(vp + int64_t(i) * D);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) st.v[x][i] = 0u;
+            }
         }
     }
 
-    static __device__ __forceinline__ void store_chunk(char *stage, const Stage &st) {
+    static __device__ __forceinline__ void store_stage(char *stage, const Stage &st) {
         const int t = threadIdx.x;
-        constexpr int KL = (KC * G::SEGS + THREADS - 1) / THREADS;
 #pragma unroll
         for (int x = 0; x < KL; ++x) {
             const int idx = t + x * THREADS;
             const int key = idx / G::SEGS, seg = idx % G::SEGS;
-            if (key < KC)
-                *reinterpret_cast<u32x4 *>(stage + (key * G::SEGS + (seg ^ kswz<D>(key))) * 16) = st.k[x];
-        }
-        const int kg = t / (D / 2), dp = t % (D / 2);
-        if (kg < 4) {
-            u32x4 lo, hi;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                lo[j] = __builtin_amdgcn_perm(st.v[2 * j + 1], st.v[2 * j], 0x05040100u);
-                hi[j] = __builtin_amdgcn_perm(st.v[2 * j + 1], st.v[2 * j], 0x07060302u);
+            if (key < KCH) {
+                const int kk = key % 32;
+                char *kb = stage + (key / 32) * G::SUB_BYTES;
+                *reinterpret_cast<u32x4 *>(kb + (kk * G::SEGS + (seg ^ kswz<D>(kk))) * 16) = st.k[x];
             }
-            char *vt = stage + G::K_BYTES;
-            *reinterpret_cast<u32x4 *>(vt + (kg * D + 2 * dp) * 16) = lo;
-            *reinterpret_cast<u32x4 *>(vt + (kg * D + 2 * dp + 1) * 16) = hi;
+        }
+#pragma unroll
+        for (int x = 0; x < VL; ++x) {
+            const int task = t + x * THREADS;
+            const int oct = task / (D / 2), dp = task % (D / 2);
+            if (oct < KCH / 8) {
+                u32x4 lo, hi;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    lo[j] = __builtin_amdgcn_perm(st.v[x][2 * j + 1], st.v[x][2 * j], 0x05040100u);
+                    hi[j] = __builtin_amdgcn_perm(st.v[x][2 * j + 1], st.v[x][2 * j], 0x07060302u);
+                }
+                char *vt = stage + (oct / 4) * G::SUB_BYTES + G::SUB_K;
+                const int kg = oct % 4;
+                *reinterpret_cast<u32x4 *>(vt + (kg * D + 2 * dp) * 16) = lo;
+                *reinterpret_cast<u32x4 *>(vt + (kg * D + 2 * dp + 1) * 16) = hi;
+            }
         }
     }
 
-    // One 32-key chunk for the RG row groups of this wave.
-    template <bool ONLINE, bool TAIL>
-    static __device__ __forceinline__ void compute_chunk(const char *stage, const bf16x8 (&qf)[RG][G::DS],
-                                                         f32x4 (&acc)[RG][G::DT], float (&lsum)[RG],
-                                                         float (&mrow)[RG], const float (&brow)[RG],
-                                                         float c) {
-        const int lane = threadIdx.x & 63;
-        const int m = lane & 15, g = lane >> 4;
-        bf16x8 ka[2][G::DS];
+    // One 32-key sub-step for NG row groups. TAIL: only keys 0..15 are valid.
+    template <int NG, bool ONLINE, bool TAIL>
+    static __device__ __forceinline__ void compute_sub(const char *sub, const bf16x8 (&qf)[ar(NG)][G::DS],
+                                                       f32x4 (&acc)[ar(NG)][G::DT], float (&lsum)[ar(NG)],
+                                                       float (&mrow)[ar(NG)], const float (&brow)[ar(NG)], float c) {
+        if constexpr (NG > 0) {
+            const int lane = threadIdx.x & 63;
+            const int m = lane & 15, g = lane >> 4;
+            bf16x8 ka[2][G::DS];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int r = 8 * (m >> 2) + 4 * j + (m & 3);
+            for (int j = 0; j < 2; ++j) {
+                const int r = 8 * (m >> 2) + 4 * j + (m & 3);
 #pragma unroll
-            for (int ds = 0; ds < G::DS; ++ds) {
-                const int seg = 4 * ds + g;
-                ka[j][ds] = *reinterpret_cast<const bf16x8 *>(stage + (r * G::SEGS + (seg ^ kswz<D>(r))) * 16);
-            }
-        }
-        bf16x8 va[G::DT];
-        const char *vt = stage + G::K_BYTES;
-#pragma unroll
-        for (int dt = 0; dt < G::DT; ++dt)
-            va[dt] = *reinterpret_cast<const bf16x8 *>(vt + (g * D + 16 * dt + m) * 16);
-
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ds = 0; ds < G::DS; ++ds) {
-                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][ds], qf[rg][ds], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][ds], qf[rg][ds], s1, 0, 0, 0);
-            }
-            // this lane: query row m of the group, keys 8g .. 8g+7 of the chunk
-            float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-            float pr[8];
-            if constexpr (!ONLINE) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(x[i], c, -brow[rg]));
-                if constexpr (TAIL) {
-                    if (g >= 2) {
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) pr[i] = 0.0f;
-                    }
+                for (int ds = 0; ds < G::DS; ++ds) {
+                    const int seg = 4 * ds + g;
+                    ka[j][ds] = *reinterpret_cast<const bf16x8 *>(sub + (r * G::SEGS + (seg ^ kswz<D>(r))) * 16);
                 }
-            } else {
-                float t[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) t[i] = x[i] * c;
-                if constexpr (TAIL) {
-                    if (g >= 2) {
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) t[i] = -__builtin_huge_valf();
-                    }
-                }
-                float cm = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])),
-                                 fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
-                cm = fmaxf(cm, __shfl_xor(cm, 16));
-                cm = fmaxf(cm, __shfl_xor(cm, 32));
-                const float mn = fmaxf(mrow[rg], cm);
-                const float alpha = __builtin_amdgcn_exp2f(mrow[rg] - mn);
-                mrow[rg] = mn;
-                lsum[rg] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < G::DT; ++dt) acc[rg][dt] *= alpha;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(t[i] - mn);
             }
-            lsum[rg] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-            bf16x8 pk;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) pk[i] = static_cast<__bf16>(pr[i]);
+            bf16x8 va[G::DT];
+            const char *vt = sub + G::SUB_K;
 #pragma unroll
             for (int dt = 0; dt < G::DT; ++dt)
-                acc[rg][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pk, acc[rg][dt], 0, 0, 0);
+                va[dt] = *reinterpret_cast<const bf16x8 *>(vt + (g * D + 16 * dt + m) * 16);
+            const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+
+#pragma unroll
+            for (int rg = 0; rg < NG; ++rg) {
+                f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ds = 0; ds < G::DS; ++ds) {
+                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][ds], qf[rg][ds], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][ds], qf[rg][ds], s1, 0, 0, 0);
+                }
+                // this lane: query row m of the group, keys 8g .. 8g+7 of the sub-step
+                const float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+                float pr[8];
+                if constexpr (!ONLINE) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(x[i], c, -brow[rg]));
+                    if constexpr (TAIL) {
+                        if (g >= 2) {
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) pr[i] = 0.0f;
+                        }
+                    }
+                } else {
+                    float t[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) t[i] = x[i] * c;
+                    if constexpr (TAIL) {
+                        if (g >= 2) {
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) t[i] = -__builtin_huge_valf();
+                        }
+                    }
+                    float cm = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])),
+                                     fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
+                    cm = fmaxf(cm, __shfl_xor(cm, 16));
+                    cm = fmaxf(cm, __shfl_xor(cm, 32));
+                    const float mn = fmaxf(mrow[rg], cm);
+                    const float alpha = __builtin_amdgcn_exp2f(mrow[rg] - mn);
+                    mrow[rg] = mn;
+                    lsum[rg] *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < G::DT; ++dt) acc[rg][dt] *= alpha;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(t[i] - mn);
+                }
+                bf16x8 pk;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pk[i] = static_cast<__bf16>(pr[i]);
+                // row sum of the bf16 weights actually used in p.v (v_dot2 with ones)
+                float l = lsum[rg];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bf16x2 two = {pk[2 * i], pk[2 * i + 1]};
+                    l = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l, false);
+                }
+                lsum[rg] = l;
+#pragma unroll
+                for (int dt = 0; dt < G::DT; ++dt)
+                    acc[rg][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pk, acc[rg][dt], 0, 0, 0);
+            }
         }
     }
 
-    template <bool ONLINE>
-    static __device__ __forceinline__ void walk(const AttnParams &p, char *smem, const uint16_t *kh,
-                                                const uint16_t *vh, int32_t e0, int32_t nhalf,
-                                                const bf16x8 (&qf)[RG][G::DS], f32x4 (&acc)[RG][G::DT],
-                                                float (&lsum)[RG], float (&mrow)[RG], const float (&brow)[RG]) {
-        const int hpb = p.block_k / 16;
-        const int nch = (nhalf + 1) / 2;
-        auto half_src = [&](int h) -> int {
-            return p.col_idx[e0 + h / hpb] * p.block_k + 16 * (h % hpb);
-        };
-        Stage st;
-        if (nch > 0) {
-            load_chunk(p, kh, vh, half_src(0), 1 < nhalf ? half_src(1) : -1, st);
-            store_chunk(smem, st);
-        }
-        if (nch > 1) load_chunk(p, kh, vh, half_src(2), 3 < nhalf ? half_src(3) : -1, st);
-        __syncthreads();
-        for (int ch = 0; ch < nch - 1; ++ch) {
-            store_chunk(smem + ((ch + 1) & 1) * G::STAGE, st);
-            if (ch + 2 < nch) {
-                const int h = 2 * (ch + 2);
-                load_chunk(p, kh, vh, half_src(h), h + 1 < nhalf ? half_src(h + 1) : -1, st);
+    template <int NG, bool ONLINE>
+    static __device__ __forceinline__ void compute_stage(const char *stage, int valid_quarters,
+                                                         const bf16x8 (&qf)[ar(NG)][G::DS], f32x4 (&acc)[ar(NG)][G::DT],
+                                                         float (&lsum)[ar(NG)], float (&mrow)[ar(NG)],
+                                                         const float (&brow)[ar(NG)], float c) {
+        if (valid_quarters >= G::QUARTERS) {
+#pragma unroll
+            for (int sb = 0; sb < G::SUB; ++sb)
+                compute_sub<NG, ONLINE, false>(stage + sb * G::SUB_BYTES, qf, acc, lsum, mrow, brow, c);
+        } else {
+#pragma unroll
+            for (int sb = 0; sb < G::SUB; ++sb) {
+                const int vq = valid_quarters - 2 * sb;
+                if (vq >= 2)
+                    compute_sub<NG, ONLINE, false>(stage + sb * G::SUB_BYTES, qf, acc, lsum, mrow, brow, c);
+                else if (vq == 1)
+                    compute_sub<NG, ONLINE, true>(stage + sb * G::SUB_BYTES, qf, acc, lsum, mrow, brow, c);
             }
-            compute_chunk<ONLINE, false>(smem + (ch & 1) * G::STAGE, qf, acc, lsum, mrow, brow, p.c);
+        }
+    }
+
+    // The block-list walk: stages of KCH keys, double-buffered in LDS, the next
+    // stage's global loads in flight while the current one is computed.
+    template <int NG, bool ONLINE>
+    static __device__ __forceinline__ void walk(const AttnParams &p, char *smem, const uint16_t *kh,
+                                                const uint16_t *vh, int32_t e0, int32_t nquart,
+                                                const bf16x8 (&qf)[ar(NG)][G::DS], f32x4 (&acc)[ar(NG)][G::DT],
+                                                float (&lsum)[ar(NG)], float (&mrow)[ar(NG)], const float (&brow)[ar(NG)]) {
+        const int nst = (nquart + G::QUARTERS - 1) / G::QUARTERS;
+        Stage st;
+        if (nst > 0) {
+            load_stage(kh, vh, stage_src(p, e0, nquart, 0), st);
+            store_stage(smem, st);
+        }
+        if (nst > 1) load_stage(kh, vh, stage_src(p, e0, nquart, 1), st);
+        __syncthreads();
+        for (int s = 0; s < nst - 1; ++s) {
+            store_stage(smem + ((s + 1) & 1) * G::STAGE, st);
+            if (s + 2 < nst) load_stage(kh, vh, stage_src(p, e0, nquart, s + 2), st);
+            compute_stage<NG, ONLINE>(smem + (s & 1) * G::STAGE, G::QUARTERS, qf, acc, lsum, mrow, brow, p.c);
             __syncthreads();
         }
-        if (nch > 0) {
-            const char *last = smem + ((nch - 1) & 1) * G::STAGE;
-            if (nhalf & 1)
-                compute_chunk<ONLINE, true>(last, qf, acc, lsum, mrow, brow, p.c);
+        if (nst > 0)
+            compute_stage<NG, ONLINE>(smem + ((nst - 1) & 1) * G::STAGE, nquart - (nst - 1) * G::QUARTERS,
+                                      qf, acc, lsum, mrow, brow, p.c);
+    }
+
+    // NG valid row groups for this wavefront, starting at group my_g0 of the query block.
+    template <int NG>
+    static __device__ __forceinline__ void tile(const AttnParams &p, char *smem, int64_t head_row0,
+                                                int32_t qb, int my_g0, const uint16_t *kh,
+                                                const uint16_t *vh, int32_t e0, int32_t nquart,
+                                                bool online, float mk) {
+        const int lane = threadIdx.x & 63;
+        const int m = lane & 15, g = lane >> 4;
+        // a wavefront without rows (NG == 0) still stages K/V and meets every barrier
+        int rows[ar(NG)];
+        bf16x8 qf[ar(NG)][G::DS];
+        f32x4 acc[ar(NG)][G::DT];
+        float lsum[ar(NG)], mrow[ar(NG)], brow[ar(NG)];
+#pragma unroll
+        for (int rg = 0; rg < NG; ++rg) {
+            rows[rg] = qb * p.block_q + (my_g0 + rg) * 16 + m;
+            const uint16_t *qr = p.q + (head_row0 + rows[rg]) * D;
+#pragma unroll
+            for (int ds = 0; ds < G::DS; ++ds)
+                qf[rg][ds] = *reinterpret_cast<const bf16x8 *>(qr + 32 * ds + 8 * g);
+#pragma unroll
+            for (int dt = 0; dt < G::DT; ++dt) acc[rg][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            lsum[rg] = 0.0f;
+            mrow[rg] = -__builtin_huge_valf();
+            brow[rg] = online ? 0.0f : p.c * p.qnorm[head_row0 + rows[rg]] * mk;
+        }
+        if (online)
+            walk<NG, true>(p, smem, kh, vh, e0, nquart, qf, acc, lsum, mrow, brow);
+        else
+            walk<NG, false>(p, smem, kh, vh, e0, nquart, qf, acc, lsum, mrow, brow);
+        if constexpr (NG > 0) {
+            // epilogue: one cross-lane reduction of the row sums, normalise, bf16, store
+#pragma unroll
+            for (int rg = 0; rg < NG; ++rg) {
+                float l = lsum[rg];
+                l += __shfl_xor(l, 16);
+                l += __shfl_xor(l, 32);
+                const float inv = 1.0f / l;
+                uint16_t *orow = p.o + (head_row0 + rows[rg]) * D;
+#pragma unroll
+                for (int dt = 0; dt < G::DT; ++dt) {
+                    __bf16 h4[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) h4[i] = static_cast<__bf16>(acc[rg][dt][i] * inv);
+                    uint2 w;
+                    w.x = uint32_t(__builtin_bit_cast(uint16_t, h4[0])) |
+                          (uint32_t(__builtin_bit_cast(uint16_t, h4[1])) << 16);
+                    w.y = uint32_t(__builtin_bit_cast(uint16_t, h4[2])) |
+                          (uint32_t(__builtin_bit_cast(uint16_t, h4[3])) << 16);
+                    *reinterpret_cast<uint2 *>(orow + 16 * dt + 4 * g) = w;
+                }
+            }
+        }
+    }
+
+    template <int NG>
+    static __device__ __forceinline__ void dispatch(int ng, const AttnParams &p, char *smem, int64_t head_row0,
+                                                    int32_t qb, int my_g0, const uint16_t *kh,
+                                                    const uint16_t *vh, int32_t e0, int32_t nquart,
+                                                    bool online, float mk) {
+        if constexpr (NG >= 0) {
+            if (ng == NG)
+                tile<NG>(p, smem, head_row0, qb, my_g0, kh, vh, e0, nquart, online, mk);
             else
-                compute_chunk<ONLINE, false>(last, qf, acc, lsum, mrow, brow, p.c);
+                dispatch<NG - 1>(ng, p, smem, head_row0, qb, my_g0, kh, vh, e0, nquart, online, mk);
         }
     }
 
     static __device__ void run(const AttnParams &p) {
-        __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE];
-        __shared__ float red[NW];
+        extern __shared__ __attribute__((aligned(16))) char smem[];
+        float *red = reinterpret_cast<float *>(smem + 2 * G::STAGE);
         const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-        const int m = lane & 15, g = lane >> 4;
 
         // XCD-aware order: consecutive workgroup ids go to different XCDs, so
         // give each XCD a contiguous range of (head, query block) work.
@@ -458,7 +622,7 @@ struct AttnKernel {
         const uint16_t *kh = p.k + head_row0 * D;
         const uint16_t *vh = p.v + head_row0 * D;
         const int32_t e0 = p.row_ptr[qb], e1 = p.row_ptr[qb + 1];
-        const int32_t nhalf = (e1 - e0) * (p.block_k / 16);
+        const int32_t nquart = (e1 - e0) * (p.block_k / 16);
         const bool online = p.eligible[hb] == 0;
 
         // bound path: largest key norm over the row's active key blocks
@@ -475,66 +639,22 @@ struct AttnKernel {
 
         const int groups = p.block_q / 16;
         for (int sub = 0; sub < groups; sub += NW * RG) {
-            const int my_g0 = sub + wave * RG;
-            int rows[RG];
-            bf16x8 qf[RG][G::DS];
-            f32x4 acc[RG][G::DT];
-            float lsum[RG], mrow[RG], brow[RG];
-#pragma unroll
-            for (int rg = 0; rg < RG; ++rg) {
-                const int grp = my_g0 + rg < groups ? my_g0 + rg : groups - 1;   // clamp idle groups
-                rows[rg] = qb * p.block_q + grp * 16 + m;
-                const uint16_t *qr = p.q + (head_row0 + rows[rg]) * D;
-#pragma unroll
-                for (int ds = 0; ds < G::DS; ++ds)
-                    qf[rg][ds] = *reinterpret_cast<const bf16x8 *>(qr + 32 * ds + 8 * g);
-#pragma unroll
-                for (int dt = 0; dt < G::DT; ++dt) acc[rg][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                lsum[rg] = 0.0f;
-                mrow[rg] = -__builtin_huge_valf();
-                brow[rg] = online ? 0.0f : p.c * p.qnorm[head_row0 + rows[rg]] * mk;
-            }
-            if (online)
-                walk<true>(p, smem, kh, vh, e0, nhalf, qf, acc, lsum, mrow, brow);
-            else
-                walk<false>(p, smem, kh, vh, e0, nhalf, qf, acc, lsum, mrow, brow);
-
-            // epilogue: one cross-lane reduction of the row sums, normalise, bf16, store
-#pragma unroll
-            for (int rg = 0; rg < RG; ++rg) {
-                float l = lsum[rg];
-                l += __shfl_xor(l, 16);
-                l += __shfl_xor(l, 32);
-                const float inv = 1.0f / l;
-                if (my_g0 + rg < groups) {
-                    uint16_t *orow = p.o + (head_row0 + rows[rg]) * D;
-#pragma unroll
-                    for (int dt = 0; dt < G::DT; ++dt) {
-                        __bf16 h4[4];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) h4[i] = static_cast<__bf16>(acc[rg][dt][i] * inv);
-                        uint2 w;
-                        w.x = uint32_t(__builtin_bit_cast(uint16_t, h4[0])) |
-                              (uint32_t(__builtin_bit_cast(uint16_t, h4[1])) << 16);
-                        w.y = uint32_t(__builtin_bit_cast(uint16_t, h4[2])) |
-                              (uint32_t(__builtin_bit_cast(uint16_t, h4[3])) << 16);
-                        *reinterpret_cast<uint2 *>(orow + 16 * dt + 4 * g) = w;
-                    }
-                }
-            }
+            // spread the sub-tile's groups over the wavefronts, RG at most each
+            const int gsub = groups - sub < NW * RG ? groups - sub : NW * RG;
+            const int base = gsub / NW, extra = gsub % NW;
+            const int ng = base + (wave < extra ? 1 : 0);
+            const int my_g0 = sub + wave * base + (wave < extra ? wave : extra);
+            dispatch<RG>(ng, p, smem, head_row0, qb, my_g0, kh, vh, e0, nquart, online, mk);
             if (sub + NW * RG < groups) __syncthreads();     // LDS reused by the next sub-tile
         }
     }
 };
 
-template <int D, int RG, int NW>
-__global__ void __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(1, 1)))
+template <int D, int RG, int NW, int KCH, int WPE>
+__global__ void __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(WPE, WPE)))
 attention_kernel(AttnParams p) {
-    AttnKernel<D, RG, NW>::run(p);
+    AttnKernel<D, RG, NW, KCH>::run(p);
 }
-
-constexpr int kRG = 4;   // 16-row groups per wavefront (64 query rows)
-constexpr int kNW = 4;   // wavefronts per workgroup (256 query rows)
 
 }  // namespace
 
@@ -585,9 +705,28 @@ int launch_bounds(const BoundsLaunch &a) {
     rp.n_kb = pl.n_kblocks;
     rp.scale = a.scale;
     rp.limit = a.bound_limit;
-    const unsigned grid2 = unsigned(nbh * pl.n_qblocks);
-    hipLaunchKernelGGL(bound_reduce_kernel, dim3(grid2), dim3(64), 0, stream, rp);
+    rp.chunks = (pl.n_qblocks + kReduceQB - 1) / kReduceQB;
+    const unsigned grid2 = unsigned(nbh * rp.chunks);
+    hipLaunchKernelGGL(bound_reduce_kernel, dim3(grid2), dim3(256), 0, stream, rp);
     err = hipGetLastError();
+    return err == hipSuccess ? 0 : int(err);
+}
+
+// Kernel configuration: 16-row groups per wavefront, wavefronts per workgroup,
+// keys per LDS stage, wavefronts per SIMD.
+template <int D, int RG, int NW, int KCH, int WPE>
+int launch_cfg(const AttnParams &p, hipStream_t stream) {
+    using K = AttnKernel<D, RG, NW, KCH>;
+    auto fn = attention_kernel<D, RG, NW, KCH, WPE>;
+    static bool attr_done = false;
+    if (!attr_done) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, K::LDS_BYTES);
+        attr_done = true;
+    }
+    const unsigned grid = unsigned(p.per_xcd * 8);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * NW), K::LDS_BYTES, stream, p);
+    const hipError_t err = hipGetLastError();
     return err == hipSuccess ? 0 : int(err);
 }
 
@@ -616,14 +755,9 @@ int launch_attention(const AttentionLaunch &a) {
     p.n_qb = pl.n_qblocks;
     p.n_kb = pl.n_kblocks;
     p.c = a.scale * kLog2e;
-    const unsigned grid = unsigned(p.per_xcd * 8);
     hipStream_t stream = static_cast<hipStream_t>(a.stream);
-    if (a.head_dim == 128)
-        hipLaunchKernelGGL((attention_kernel<128, kRG, kNW>), dim3(grid), dim3(64 * kNW), 0, stream, p);
-    else
-        hipLaunchKernelGGL((attention_kernel<64, kRG, kNW>), dim3(grid), dim3(64 * kNW), 0, stream, p);
-    const hipError_t err = hipGetLastError();
-    return err == hipSuccess ? 0 : int(err);
+    if (a.head_dim == 128) return launch_cfg<128, FSA_RG, FSA_NW, FSA_KCH, FSA_WPE>(p, stream);
+    return launch_cfg<64, FSA_RG, FSA_NW, FSA_KCH, FSA_WPE>(p, stream);
 }
 
 }  // namespace fsa
