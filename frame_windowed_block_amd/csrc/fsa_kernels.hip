@@ -58,6 +58,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Read-only device data addressed uniformly: loads through the constant address
+// space are selected as scalar (SMEM) loads.
+typedef __attribute__((address_space(4))) const int32_t cint32;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -313,13 +316,48 @@ struct AttnKernel {
         uint32_t v[VL][8];
     };
 
-    // Source key of each 16-key tile of a stage (-1: past the end of the row).
-    // Named fields, not an array: a lane-varying pick must stay a select chain
-    // rather than become a dynamically indexed (scratch) array.
+    // Where the 16-key tiles of one stage come from: the raw list entries
+    // (col_idx) and tile offsets; the key index col * bk + 16 * j is formed
+    // only when the stage is loaded, so the scalar loads of the entries are
+    // in flight for a whole stage before they are needed. Named fields, not
+    // arrays: a lane-varying pick must stay a select chain.
     static_assert(G::QUARTERS == 2 || G::QUARTERS == 4, "stages of 32 or 64 keys");
     struct Src {
-        int q0, q1, q2, q3;
+        int c0, c1, c2, c3;     // list entries (block indices), -1 past the row end
+        int j0, j1, j2, j3;     // 16-key tile inside the block
     };
+    // Cursor over the row's 16-key tiles: list position e and tile j in its block.
+    struct Cursor {
+        int32_t e, j;
+    };
+
+    static __device__ __forceinline__ Src next_src(const cint32 *col, Cursor &cur, int32_t e1, int hpb) {
+        Src s;
+        auto one = [&](int &c, int &j) {
+            if (cur.e < e1) {
+                c = col[cur.e];
+                j = cur.j;
+                if (++cur.j == hpb) {
+                    cur.j = 0;
+                    ++cur.e;
+                }
+            } else {
+                c = -1;
+                j = 0;
+            }
+        };
+        one(s.c0, s.j0);
+        one(s.c1, s.j1);
+        if constexpr (G::QUARTERS > 2) {
+            one(s.c2, s.j2);
+            one(s.c3, s.j3);
+        } else {
+            s.c2 = s.c3 = -1;
+            s.j2 = s.j3 = 0;
+        }
+        return s;
+    }
+
     // src[j] for a lane-varying j, computed on values (a select on field
     // addresses would turn the struct into a dynamically indexed stack array)
     static __device__ __forceinline__ int pick(int j, int q0, int q1, int q2, int q3) {
@@ -328,24 +366,13 @@ struct AttnKernel {
         return (G::QUARTERS == 2 || j < 2) ? lo : hi;
     }
 
-    static __device__ __forceinline__ Src stage_src(const AttnParams &p, int32_t e0, int nquart, int st) {
-        const int hpb = p.block_k / 16;
-        auto one = [&](int j) -> int {
-            const int h = st * G::QUARTERS + j;
-            return h < nquart ? p.col_idx[e0 + h / hpb] * p.block_k + 16 * (h % hpb) : -1;
-        };
-        Src s;
-        s.q0 = one(0);
-        s.q1 = one(1);
-        s.q2 = G::QUARTERS > 2 ? one(2) : -1;
-        s.q3 = G::QUARTERS > 2 ? one(3) : -1;
-        return s;
-    }
-
     static __device__ __forceinline__ void load_stage(const uint16_t *kh, const uint16_t *vh,
-                                                      const Src src, Stage &st) {
+                                                      const Src src, int bk, Stage &st) {
         const int t = threadIdx.x;
-        const int s0 = src.q0, s1 = src.q1, s2 = src.q2, s3 = src.q3;
+        const int s0 = src.c0 < 0 ? -1 : src.c0 * bk + 16 * src.j0;
+        const int s1 = src.c1 < 0 ? -1 : src.c1 * bk + 16 * src.j1;
+        const int s2 = src.c2 < 0 ? -1 : src.c2 * bk + 16 * src.j2;
+        const int s3 = src.c3 < 0 ? -1 : src.c3 * bk + 16 * src.j3;
 #pragma unroll
         for (int x = 0; x < KL; ++x) {
             const int idx = t + x * THREADS;
@@ -514,20 +541,27 @@ struct AttnKernel {
     // stage's global loads in flight while the current one is computed.
     template <int NG, bool ONLINE>
     static __device__ __forceinline__ void walk(const AttnParams &p, char *smem, const uint16_t *kh,
-                                                const uint16_t *vh, int32_t e0, int32_t nquart,
+                                                const uint16_t *vh, int32_t e0, int32_t e1, int32_t nquart,
                                                 const bf16x8 (&qf)[ar(NG)][G::DS], f32x4 (&acc)[ar(NG)][G::DT],
                                                 float (&lsum)[ar(NG)], float (&mrow)[ar(NG)], const float (&brow)[ar(NG)]) {
         const int nst = (nquart + G::QUARTERS - 1) / G::QUARTERS;
+        const int hpb = p.block_k / 16;
+        const cint32 *col = (const cint32 *)(p.col_idx);
+        Cursor cur{e0, 0};
         Stage st;
         if (nst > 0) {
-            load_stage(kh, vh, stage_src(p, e0, nquart, 0), st);
+            load_stage(kh, vh, next_src(col, cur, e1, hpb), p.block_k, st);
             store_stage(smem, st);
         }
-        if (nst > 1) load_stage(kh, vh, stage_src(p, e0, nquart, 1), st);
+        if (nst > 1) load_stage(kh, vh, next_src(col, cur, e1, hpb), p.block_k, st);
+        Src nxt = next_src(col, cur, e1, hpb);           // stage 2, fetched a stage early
         __syncthreads();
         for (int s = 0; s < nst - 1; ++s) {
             store_stage(smem + ((s + 1) & 1) * G::STAGE, st);
-            if (s + 2 < nst) load_stage(kh, vh, stage_src(p, e0, nquart, s + 2), st);
+            if (s + 2 < nst) {
+                load_stage(kh, vh, nxt, p.block_k, st);
+                nxt = next_src(col, cur, e1, hpb);
+            }
             compute_stage<NG, ONLINE>(smem + (s & 1) * G::STAGE, G::QUARTERS, qf, acc, lsum, mrow, brow, p.c);
             __syncthreads();
         }
@@ -540,7 +574,7 @@ struct AttnKernel {
     template <int NG>
     static __device__ __forceinline__ void tile(const AttnParams &p, char *smem, int64_t head_row0,
                                                 int32_t qb, int my_g0, const uint16_t *kh,
-                                                const uint16_t *vh, int32_t e0, int32_t nquart,
+                                                const uint16_t *vh, int32_t e0, int32_t e1, int32_t nquart,
                                                 bool online, float mk) {
         const int lane = threadIdx.x & 63;
         const int m = lane & 15, g = lane >> 4;
@@ -563,9 +597,9 @@ struct AttnKernel {
             brow[rg] = online ? 0.0f : p.c * p.qnorm[head_row0 + rows[rg]] * mk;
         }
         if (online)
-            walk<NG, true>(p, smem, kh, vh, e0, nquart, qf, acc, lsum, mrow, brow);
+            walk<NG, true>(p, smem, kh, vh, e0, e1, nquart, qf, acc, lsum, mrow, brow);
         else
-            walk<NG, false>(p, smem, kh, vh, e0, nquart, qf, acc, lsum, mrow, brow);
+            walk<NG, false>(p, smem, kh, vh, e0, e1, nquart, qf, acc, lsum, mrow, brow);
         if constexpr (NG > 0) {
             // epilogue: one cross-lane reduction of the row sums, normalise, bf16, store
 #pragma unroll
@@ -594,13 +628,13 @@ struct AttnKernel {
     template <int NG>
     static __device__ __forceinline__ void dispatch(int ng, const AttnParams &p, char *smem, int64_t head_row0,
                                                     int32_t qb, int my_g0, const uint16_t *kh,
-                                                    const uint16_t *vh, int32_t e0, int32_t nquart,
+                                                    const uint16_t *vh, int32_t e0, int32_t e1, int32_t nquart,
                                                     bool online, float mk) {
         if constexpr (NG >= 0) {
             if (ng == NG)
-                tile<NG>(p, smem, head_row0, qb, my_g0, kh, vh, e0, nquart, online, mk);
+                tile<NG>(p, smem, head_row0, qb, my_g0, kh, vh, e0, e1, nquart, online, mk);
             else
-                dispatch<NG - 1>(ng, p, smem, head_row0, qb, my_g0, kh, vh, e0, nquart, online, mk);
+                dispatch<NG - 1>(ng, p, smem, head_row0, qb, my_g0, kh, vh, e0, e1, nquart, online, mk);
         }
     }
 
@@ -644,7 +678,7 @@ struct AttnKernel {
             const int base = gsub / NW, extra = gsub % NW;
             const int ng = base + (wave < extra ? 1 : 0);
             const int my_g0 = sub + wave * base + (wave < extra ? wave : extra);
-            dispatch<RG>(ng, p, smem, head_row0, qb, my_g0, kh, vh, e0, nquart, online, mk);
+            dispatch<RG>(ng, p, smem, head_row0, qb, my_g0, kh, vh, e0, e1, nquart, online, mk);
             if (sub + NW * RG < groups) __syncthreads();     // LDS reused by the next sub-tile
         }
     }
