@@ -289,6 +289,18 @@ __device__ __forceinline__ int kswz(int r) {
 
 constexpr int ar(int n) { return n > 0 ? n : 1; }   // array extent for n row groups
 
+// Workgroup barrier for LDS hand-offs. __syncthreads() also waits for every
+// outstanding global load (vmcnt(0)), which would drain the next stage's
+// prefetch at each stage boundary. Here: a compiler-only fence (no reordering
+// of memory accesses across the barrier), this wave's LDS accesses complete
+// (lgkmcnt(0)), then s_barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Query-block order inside a head: frames from the middle outwards, so the
 // first workgroups of a head share their key window in L2 and the cheaper edge
 // frames (fewer visible frames) run last.
@@ -555,7 +567,7 @@ struct AttnKernel {
         }
         if (nst > 1) load_stage(kh, vh, next_src(col, cur, e1, hpb), p.block_k, st);
         Src nxt = next_src(col, cur, e1, hpb);           // stage 2, fetched a stage early
-        __syncthreads();
+        lds_barrier();
         for (int s = 0; s < nst - 1; ++s) {
             store_stage(smem + ((s + 1) & 1) * G::STAGE, st);
             if (s + 2 < nst) {
@@ -563,7 +575,7 @@ struct AttnKernel {
                 nxt = next_src(col, cur, e1, hpb);
             }
             compute_stage<NG, ONLINE>(smem + (s & 1) * G::STAGE, G::QUARTERS, qf, acc, lsum, mrow, brow, p.c);
-            __syncthreads();
+            lds_barrier();
         }
         if (nst > 0)
             compute_stage<NG, ONLINE>(smem + ((nst - 1) & 1) * G::STAGE, nquart - (nst - 1) * G::QUARTERS,
@@ -666,7 +678,7 @@ struct AttnKernel {
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) mk = fmaxf(mk, __shfl_xor(mk, off));
             if (lane == 0) red[wave] = mk;
-            __syncthreads();
+            lds_barrier();
 #pragma unroll
             for (int w = 0; w < NW; ++w) mk = fmaxf(mk, red[w]);
         }
@@ -679,7 +691,7 @@ struct AttnKernel {
             const int ng = base + (wave < extra ? 1 : 0);
             const int my_g0 = sub + wave * base + (wave < extra ? wave : extra);
             dispatch<RG>(ng, p, smem, head_row0, qb, my_g0, kh, vh, e0, e1, nquart, online, mk);
-            if (sub + NW * RG < groups) __syncthreads();     // LDS reused by the next sub-tile
+            if (sub + NW * RG < groups) lds_barrier();     // LDS reused by the next sub-tile
         }
     }
 };
