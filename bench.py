@@ -12,8 +12,11 @@ device synchronisations. Prints ONE JSON line:
   K steps, in TFLOP/s, and pct_of_peak against the bf16 dense MFMA peak;
 * roofline: fsa_attention (the dominant kernel, MFMA-bound) with its mean
   duration from HIP events recorded on its launch stream around each launch;
-* cpu_baseline: the fp64 oracle (not tuned) timed on one head of the same
-  workload on the host cores, scaled to the same unit.
+* cpu_baseline: the fp64 oracle (not tuned) timed on four heads of the same
+  workload on the host cores, scaled to the same unit;
+* roofline.traffic: HBM bytes per launch from the committed rocprofv3
+  FETCH_SIZE / WRITE_SIZE passes (profiles/traffic.json), reported only while
+  the kernel source still matches the one those counters were taken on.
 
 Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -32,6 +35,22 @@ if ROOT not in sys.path:
 METRIC = "effective TFLOP/s on active blocks + % of bf16 MFMA peak, 25k-token SR attn"
 PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E
+KERNEL_SOURCE = os.path.join(ROOT, "frame_windowed_block_amd", "csrc", "fsa_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    passes (copy-calibrated), or None when they were taken on other kernel source."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)[kernel][workload]
+        with open(KERNEL_SOURCE, "rb") as fh:
+            sha = hashlib.sha256(fh.read()).hexdigest()
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["traffic_bytes"] if rec.get("kernel_source_sha256") == sha else None
 
 
 def parse():
@@ -197,7 +216,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("fsa_attention", wl.name),
             "mean_ms": round(attn_mean, 5),
             "p10_ms": round(float(np.percentile(attn_ms, 10)), 5),
             "p90_ms": round(float(np.percentile(attn_ms, 90)), 5),
@@ -207,6 +226,8 @@ def main():
             "mean_ms": round(float(bnd_ms.mean()), 5),
             "gbps": round(bounds_bytes / (float(bnd_ms.mean()) * 1e-3) / 1e9, 1),
             "peak_gbps": PEAK_HBM_GBPS,
+            "algorithmic_bytes": bounds_bytes,
+            "traffic": measured_traffic("fsa_bounds_norms", wl.name),
         },
     }
     if not args.no_cpu_baseline:

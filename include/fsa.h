@@ -23,7 +23,7 @@
  *                  take the standard online softmax inside the same kernel
  *                  (section "Giải phóng Softmax", Fig. 4). A head range lets a
  *                  caller run independent head groups that each see exactly the
- *                  ungrouped mask (section on hiding collective overhead).
+ *                  ungrouped mask (section "Ẩn đi các tập lệnh tập thể (Collective)").
  *
  * Notation: B batch, H heads, F frames, T tokens per frame, N = F*T tokens,
  * D head dim, w window half-width (frames), r reference frame, bq / bk query /

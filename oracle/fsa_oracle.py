@@ -11,11 +11,12 @@ Sources (the pages reporting the HeyGen / Google Cloud Avatar IV port):
 * [vi:Mask]    aihot.vn, "HeyGen tối ưu hóa mô hình Avatar IV trên Google
                Cloud Trillium TPU", section "Xóa bỏ mặt nạ (Mask)" and Fig. 3.
 * [vi:Softmax] same page, section "Giải phóng Softmax" and Fig. 4.
-* [vi:Coll]    same page, section on hiding collective overhead (head groups
-               keep the token order, so each group sees the ungrouped mask).
+* [vi:Coll]    same page, section "Ẩn đi các tập lệnh tập thể (Collective)" (head
+               groups keep the token order, so each group sees the ungrouped mask).
 * [uk:Mask], [uk:Softmax]  bib.com.ua, "HeyGen прискорила Avatar IV на TPU у
-               1,86 раза", sections on removing the sparse-attention mask and
-               on breaking the softmax serial chain (corroborating text).
+               1,86 раза", sections "Маску sparse attention прибрали
+               конструктивно" and "Як розірвали послідовний ланцюг softmax"
+               (corroborating text).
 
 What the method computes, in the pages' terms: each query frame attends to a
 window of neighbouring frames plus one global reference frame [vi:Mask]; the
