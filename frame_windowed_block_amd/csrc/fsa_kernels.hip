@@ -378,6 +378,16 @@ struct AttnKernel {
         return (G::QUARTERS == 2 || j < 2) ? lo : hi;
     }
 
+    // Each wave's loads of a stage fall in one 16-key quarter per (x) slot: a
+    // wave-wide K load covers 64 / SEGS consecutive keys and a V load one key
+    // octet, both inside one quarter. The quarter index is therefore uniform
+    // over the wave and is made scalar, so the source pick is a scalar select.
+    static_assert(64 % G::SEGS == 0 && 16 % (64 / G::SEGS) == 0, "wave-wide K load inside one quarter");
+    static_assert((D / 2) % 64 == 0 || 64 % (D / 2) == 0, "wave-wide V load inside one quarter");
+
+    // FULL: every quarter of the stage lies inside the row (all but possibly
+    // the last stage), so no load needs a validity check.
+    template <bool FULL>
     static __device__ __forceinline__ void load_stage(const uint16_t *kh, const uint16_t *vh,
                                                       const Src src, int bk, Stage &st) {
         const int t = threadIdx.x;
@@ -389,8 +399,9 @@ struct AttnKernel {
         for (int x = 0; x < KL; ++x) {
             const int idx = t + x * THREADS;
             const int key = idx / G::SEGS, seg = idx % G::SEGS;
-            const int qs = key < KCH ? pick(key / 16, s0, s1, s2, s3) : -1;
-            if (qs >= 0)
+            const int quarter = __builtin_amdgcn_readfirstlane(key / 16);
+            const int qs = key < KCH ? pick(quarter, s0, s1, s2, s3) : -1;
+            if (FULL || qs >= 0)
                 st.k[x] = *reinterpret_cast<const u32x4 *>(kh + int64_t(qs + key % 16) * D + seg * 8);
             else
                 st.k[x] = u32x4{0u, 0u, 0u, 0u};
@@ -399,8 +410,9 @@ struct AttnKernel {
         for (int x = 0; x < VL; ++x) {
             const int task = t + x * THREADS;
             const int oct = task / (D / 2), dp = task % (D / 2);
-            const int qs = oct < KCH / 8 ? pick(oct / 2, s0, s1, s2, s3) : -1;
-            if (qs >= 0) {
+            const int quarter = __builtin_amdgcn_readfirstlane(oct / 2);
+            const int qs = oct < KCH / 8 ? pick(quarter, s0, s1, s2, s3) : -1;
+            if (FULL || qs >= 0) {
                 const uint16_t *vp = vh + int64_t(qs + 8 * (oct & 1)) * D + 2 * dp;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) st.v[x][i] = *reinterpret_cast<const uint32_t *>(vp + int64_t(i) * D);
@@ -445,7 +457,7 @@ struct AttnKernel {
     // One 32-key sub-step for NG row groups. TAIL: only keys 0..15 are valid.
     template <int NG, bool ONLINE, bool TAIL>
     static __device__ __forceinline__ void compute_sub(const char *sub, const bf16x8 (&qf)[ar(NG)][G::DS],
-                                                       f32x4 (&acc)[ar(NG)][G::DT], float (&lsum)[ar(NG)],
+                                                       f32x4 (&acc)[ar(NG)][G::DT], f32x4 (&lsum)[ar(NG)],
                                                        float (&mrow)[ar(NG)], const float (&brow)[ar(NG)], float c) {
         if constexpr (NG > 0) {
             const int lane = threadIdx.x & 63;
@@ -465,7 +477,9 @@ struct AttnKernel {
 #pragma unroll
             for (int dt = 0; dt < G::DT; ++dt)
                 va[dt] = *reinterpret_cast<const bf16x8 *>(vt + (g * D + 16 * dt + m) * 16);
-            const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+            bf16x8 ones8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ones8[i] = static_cast<__bf16>(1.0f);
 
 #pragma unroll
             for (int rg = 0; rg < NG; ++rg) {
@@ -513,14 +527,9 @@ struct AttnKernel {
                 bf16x8 pk;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) pk[i] = static_cast<__bf16>(pr[i]);
-                // row sum of the bf16 weights actually used in p.v (v_dot2 with ones)
-                float l = lsum[rg];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bf16x2 two = {pk[2 * i], pk[2 * i + 1]};
-                    l = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l, false);
-                }
-                lsum[rg] = l;
+                // row sums of the bf16 weights actually used in p.v, on the matrix
+                // unit: a ones "V^T" tile gives every output row the sum over keys
+                lsum[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pk, lsum[rg], 0, 0, 0);
 #pragma unroll
                 for (int dt = 0; dt < G::DT; ++dt)
                     acc[rg][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pk, acc[rg][dt], 0, 0, 0);
@@ -531,7 +540,7 @@ struct AttnKernel {
     template <int NG, bool ONLINE>
     static __device__ __forceinline__ void compute_stage(const char *stage, int valid_quarters,
                                                          const bf16x8 (&qf)[ar(NG)][G::DS], f32x4 (&acc)[ar(NG)][G::DT],
-                                                         float (&lsum)[ar(NG)], float (&mrow)[ar(NG)],
+                                                         f32x4 (&lsum)[ar(NG)], float (&mrow)[ar(NG)],
                                                          const float (&brow)[ar(NG)], float c) {
         if (valid_quarters >= G::QUARTERS) {
 #pragma unroll
@@ -555,23 +564,30 @@ struct AttnKernel {
     static __device__ __forceinline__ void walk(const AttnParams &p, char *smem, const uint16_t *kh,
                                                 const uint16_t *vh, int32_t e0, int32_t e1, int32_t nquart,
                                                 const bf16x8 (&qf)[ar(NG)][G::DS], f32x4 (&acc)[ar(NG)][G::DT],
-                                                float (&lsum)[ar(NG)], float (&mrow)[ar(NG)], const float (&brow)[ar(NG)]) {
+                                                f32x4 (&lsum)[ar(NG)], float (&mrow)[ar(NG)], const float (&brow)[ar(NG)]) {
         const int nst = (nquart + G::QUARTERS - 1) / G::QUARTERS;
         const int hpb = p.block_k / 16;
         const cint32 *col = (const cint32 *)(p.col_idx);
         Cursor cur{e0, 0};
         Stage st;
+        const bool last_full = nquart % G::QUARTERS == 0;
+        auto load = [&](int stage_idx, const Src &src) {
+            if (stage_idx < nst - 1 || last_full)
+                load_stage<true>(kh, vh, src, p.block_k, st);
+            else
+                load_stage<false>(kh, vh, src, p.block_k, st);
+        };
         if (nst > 0) {
-            load_stage(kh, vh, next_src(col, cur, e1, hpb), p.block_k, st);
+            load(0, next_src(col, cur, e1, hpb));
             store_stage(smem, st);
         }
-        if (nst > 1) load_stage(kh, vh, next_src(col, cur, e1, hpb), p.block_k, st);
+        if (nst > 1) load(1, next_src(col, cur, e1, hpb));
         Src nxt = next_src(col, cur, e1, hpb);           // stage 2, fetched a stage early
         lds_barrier();
         for (int s = 0; s < nst - 1; ++s) {
             store_stage(smem + ((s + 1) & 1) * G::STAGE, st);
             if (s + 2 < nst) {
-                load_stage(kh, vh, nxt, p.block_k, st);
+                load(s + 2, nxt);
                 nxt = next_src(col, cur, e1, hpb);
             }
             compute_stage<NG, ONLINE>(smem + (s & 1) * G::STAGE, G::QUARTERS, qf, acc, lsum, mrow, brow, p.c);
@@ -594,7 +610,8 @@ struct AttnKernel {
         int rows[ar(NG)];
         bf16x8 qf[ar(NG)][G::DS];
         f32x4 acc[ar(NG)][G::DT];
-        float lsum[ar(NG)], mrow[ar(NG)], brow[ar(NG)];
+        f32x4 lsum[ar(NG)];            // row sums (all four entries equal; see compute_sub)
+        float mrow[ar(NG)], brow[ar(NG)];
 #pragma unroll
         for (int rg = 0; rg < NG; ++rg) {
             rows[rg] = qb * p.block_q + (my_g0 + rg) * 16 + m;
@@ -604,7 +621,7 @@ struct AttnKernel {
                 qf[rg][ds] = *reinterpret_cast<const bf16x8 *>(qr + 32 * ds + 8 * g);
 #pragma unroll
             for (int dt = 0; dt < G::DT; ++dt) acc[rg][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            lsum[rg] = 0.0f;
+            lsum[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
             mrow[rg] = -__builtin_huge_valf();
             brow[rg] = online ? 0.0f : p.c * p.qnorm[head_row0 + rows[rg]] * mk;
         }
@@ -613,13 +630,10 @@ struct AttnKernel {
         else
             walk<NG, false>(p, smem, kh, vh, e0, e1, nquart, qf, acc, lsum, mrow, brow);
         if constexpr (NG > 0) {
-            // epilogue: one cross-lane reduction of the row sums, normalise, bf16, store
+            // epilogue: normalise by the row sum, bf16, store
 #pragma unroll
             for (int rg = 0; rg < NG; ++rg) {
-                float l = lsum[rg];
-                l += __shfl_xor(l, 16);
-                l += __shfl_xor(l, 32);
-                const float inv = 1.0f / l;
+                const float inv = 1.0f / lsum[rg][0];
                 uint16_t *orow = p.o + (head_row0 + rows[rg]) * D;
 #pragma unroll
                 for (int dt = 0; dt < G::DT; ++dt) {
