@@ -15,52 +15,46 @@
 // the last block of each head writes the head's eligibility ([vi:Softmax]:
 // eligibility is checked per attention head).
 //
-// fsa_attention is one kernel: one workgroup per (batch, head, query block).
-// It walks the query block's active key-block list once, window and reference
-// frame alike ([vi:Mask]: one pass covers the whole mask), in 32-key chunks
-// that may join the 16-key tail of one block to the head of the next; no chunk
-// needs a mask predicate, and an odd count of 16-key tiles leaves one half
-// chunk at the very end. Per chunk:
-//   S^T = K Q^T       bf16 MFMA 16x16x32 (K rows permuted so that each lane
-//                     ends up holding 8 consecutive keys of one query row)
+// fsa_attention is one kernel: one workgroup per (batch, head, query block),
+// eight wavefronts of 32 query rows each. It walks the query block's active
+// key-block list once, window and reference frame alike ([vi:Mask]: one pass
+// covers the whole mask), in 32-key sub-steps that may join the 16-key tail
+// of one block to the head of the next; no sub-step needs a mask predicate,
+// and an odd count of 16-key tiles leaves one half sub-step at the very end.
+// Per sub-step and wavefront:
+//   S^T = K Q^T       bf16 MFMA 32x32x16 (K rows permuted so that each lane
+//                     ends up holding 16 keys of one query row, in the order
+//                     the p.v operand wants them)
 //   P   = exp2(S * scale * log2e - B_i * log2e)
 //                     B_i = scale * ||q_i|| * max kmax over the row's active
 //                     key blocks, fixed before the loop ([vi:Softmax]); no
 //                     running max, no rescale
-//   O^T += V^T P^T    bf16 MFMA 16x16x32 with V staged transposed in LDS
-// Heads whose bound is too loose run the same walk with the standard running
-// max and rescale instead ([vi:Softmax], Fig. 4), chosen by a branch that is
-// uniform over the workgroup.
+//   O^T += V^T P^T    bf16 MFMA 32x32x16, V^T read from row-major V in LDS
+//                     with the transposing LDS reads
+// The scores of sub-step j + 1 are computed in the same step as the weights
+// and p.v of sub-step j. Heads whose bound is too loose run the same walk
+// with the standard running max and rescale instead ([vi:Softmax], Fig. 4),
+// chosen by a branch that is uniform over the workgroup.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "fsa_internal.h"
-
-// Attention kernel configuration (overridable at build time for tuning sweeps).
-#ifndef FSA_RG
-#define FSA_RG 2      // 16-row query groups per wavefront
-#endif
-#ifndef FSA_NW
-#define FSA_NW 8      // wavefronts per workgroup
-#endif
-#ifndef FSA_KCH
-#define FSA_KCH 64    // keys per LDS stage
-#endif
-#ifndef FSA_WPE
-#define FSA_WPE 2     // wavefronts per SIMD the registers are budgeted for
-#endif
 
 namespace fsa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Read-only device data addressed uniformly: loads through the constant address
 // space are selected as scalar (SMEM) loads.
 typedef __attribute__((address_space(4))) const int32_t cint32;
+typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
+typedef short v8s __attribute__((__vector_size__(8 * sizeof(short))));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -264,30 +258,29 @@ struct AttnParams {
     float c;            // scale * log2(e)
 };
 
-// Geometry of one LDS stage: KCH keys = KCH/32 "sub-steps" of 32 keys, each
-// holding K [32][D] (16-byte segments swizzled) and V^T [4 key octets][D][8].
-template <int D, int KCH>
+// Geometry of one LDS stage: 64 keys = two 32-key sub-steps, each holding K
+// segment-major, [D/8 segments][32 keys][8 d] (16 bytes per key and segment),
+// then V row-major with rows padded to VRS bytes.
+template <int D>
 struct Geo {
-    static constexpr int SEGS = D / 8;             // 16-byte segments per K row
-    static constexpr int DS = D / 32;              // q.k MFMA steps over d
-    static constexpr int DT = D / 16;              // 16-wide output column tiles
-    static constexpr int SUB = KCH / 32;           // 32-key p.v MFMA steps per stage
-    static constexpr int QUARTERS = KCH / 16;      // 16-key tiles per stage
+    static constexpr int SEGS = D / 8;             // 16-byte segments per K / V row
+    static constexpr int KS = D / 16;              // q.k MFMA steps over d (16 each)
+    static constexpr int DT = D / 32;              // 32-wide output column tiles
     static constexpr int SUB_K = 32 * D * 2;
-    static constexpr int SUB_BYTES = 2 * SUB_K;    // K then V^T
-    static constexpr int STAGE = SUB * SUB_BYTES;
+    // V rows padded by 64 bytes: the transposing reads of four consecutive
+    // rows then fall in four different 64-byte bank groups
+    static constexpr int VRS = 2 * D + 64;
+    static constexpr int SUB_V = 32 * VRS;
+    static constexpr int SUB_BYTES = SUB_K + SUB_V;
+    static constexpr int STAGE = 2 * SUB_BYTES;
 };
 
-// Swizzle of K's 16-byte segments: row r stores segment s at s ^ kswz(r). With
-// the permuted row order used by the q.k fragments, the 16 lanes of a quarter
-// wave read 16 different segments of their rows: no LDS bank conflicts.
-template <int D>
-__device__ __forceinline__ int kswz(int r) {
-    if constexpr (D == 128) return (r & 3) | (((r >> 3) & 3) << 2);
-    else return (r & 3) | (((r >> 3) & 1) << 2);
-}
-
-constexpr int ar(int n) { return n > 0 ? n : 1; }   // array extent for n row groups
+// Key order of the q.k product. Row n of the 32x32 MFMA's K operand holds key
+// sigma(n) of the sub-step (bits 2 and 3 of n swapped). The result registers
+// of lane (n, h = lane / 32) then hold, for query n, keys 8h..8h+7 in
+// registers 0..7 and keys 16+8h..16+8h+7 in registers 8..15: after exp and
+// rounding, exactly the two p.v B operands (k-steps of 16 keys) of that lane.
+__device__ __forceinline__ int sigma(int n) { return (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1); }
 
 // Workgroup barrier for LDS hand-offs. __syncthreads() also waits for every
 // outstanding global load (vmcnt(0)), which would drain the next stage's
@@ -311,32 +304,40 @@ __device__ __forceinline__ int32_t rank_to_qblock(int32_t rank, int32_t frames, 
     return f * qpf + qi;
 }
 
-// D: head dim. RG: 16-row groups per wavefront. NW: wavefronts per workgroup.
-// KCH: keys per LDS stage (32 or 64).
-template <int D, int RG, int NW, int KCH>
+// Buffer descriptor over one head's K or V slab (raw, unswizzled, 32-bit data).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
+
+// One workgroup per (batch, head, query block): 8 wavefronts, two per SIMD,
+// each owning a tile of 32 query rows (Q fragments and the fp32 output
+// accumulators in registers). Stages of 64 keys rotate through three LDS
+// buffers.
+template <int D>
 struct AttnKernel {
-    using G = Geo<D, KCH>;
+    using G = Geo<D>;
+    static constexpr int NW = 8;
     static constexpr int THREADS = 64 * NW;
-    static constexpr int KL = (KCH * G::SEGS + THREADS - 1) / THREADS;            // K segments / thread
-    static constexpr int VTASKS = (KCH / 8) * (D / 2);
-    static constexpr int VL = (VTASKS + THREADS - 1) / THREADS;                   // V tasks / thread
-    static constexpr int LDS_BYTES = 2 * G::STAGE + 64;
+    static constexpr int KL = 64 * G::SEGS / THREADS;   // 16-byte K (and V) loads per thread and stage
+    static constexpr int RPI = 64 / G::SEGS;            // V rows per wave-wide load
+    static constexpr int NBUF = 3;
+    static constexpr int LDS_BYTES = NBUF * G::STAGE;
+    static_assert(KL >= 1 && NW * KL * 64 == 64 * G::SEGS, "loads cover the stage");
 
     // Global -> register staging of one stage.
     struct Stage {
-        u32x4 k[KL];
-        uint32_t v[VL][8];
+        u32x4 k[KL], v[KL];
     };
 
-    // Where the 16-key tiles of one stage come from: the raw list entries
-    // (col_idx) and tile offsets; the key index col * bk + 16 * j is formed
-    // only when the stage is loaded, so the scalar loads of the entries are
-    // in flight for a whole stage before they are needed. Named fields, not
-    // arrays: a lane-varying pick must stay a select chain.
-    static_assert(G::QUARTERS == 2 || G::QUARTERS == 4, "stages of 32 or 64 keys");
+    // The four 16-key tiles of a stage: list entries (block indices, loaded
+    // by scalar loads) and tile positions inside their blocks. The byte
+    // offsets are formed only when the stage is loaded, one stage later, so
+    // the scalar loads are in flight meanwhile. Tiles past the row end repeat
+    // the row's last tile: they are loaded but never weighted.
     struct Src {
-        int c0, c1, c2, c3;     // list entries (block indices), -1 past the row end
-        int j0, j1, j2, j3;     // 16-key tile inside the block
+        int32_t c0, c1, c2, c3;
+        int32_t j0, j1, j2, j3;
     };
     // Cursor over the row's 16-key tiles: list position e and tile j in its block.
     struct Cursor {
@@ -344,329 +345,356 @@ struct AttnKernel {
     };
 
     static __device__ __forceinline__ Src next_src(const cint32 *col, Cursor &cur, int32_t e1, int hpb) {
-        Src s;
-        auto one = [&](int &c, int &j) {
-            if (cur.e < e1) {
-                c = col[cur.e];
-                j = cur.j;
-                if (++cur.j == hpb) {
-                    cur.j = 0;
-                    ++cur.e;
-                }
-            } else {
-                c = -1;
-                j = 0;
-            }
+        auto one = [&](int32_t &c, int32_t &j) {
+            c = col[cur.e < e1 ? cur.e : e1 - 1];
+            j = cur.j;
+            const bool wrap = cur.j + 1 == hpb;
+            cur.e += wrap ? 1 : 0;
+            cur.j = wrap ? 0 : cur.j + 1;
         };
+        Src s;
         one(s.c0, s.j0);
         one(s.c1, s.j1);
-        if constexpr (G::QUARTERS > 2) {
-            one(s.c2, s.j2);
-            one(s.c3, s.j3);
-        } else {
-            s.c2 = s.c3 = -1;
-            s.j2 = s.j3 = 0;
-        }
+        one(s.c2, s.j2);
+        one(s.c3, s.j3);
         return s;
     }
 
-    // src[j] for a lane-varying j, computed on values (a select on field
-    // addresses would turn the struct into a dynamically indexed stack array)
-    static __device__ __forceinline__ int pick(int j, int q0, int q1, int q2, int q3) {
-        const int lo = j == 0 ? q0 : q1;
-        const int hi = j == 2 ? q2 : q3;
-        return (G::QUARTERS == 2 || j < 2) ? lo : hi;
+    // tile j (wave-uniform) of a stage, as a scalar select chain on values (a
+    // select on field addresses would make the struct a dynamically indexed
+    // array in scratch memory)
+    static __device__ __forceinline__ int32_t pick(int j, int32_t o0, int32_t o1, int32_t o2, int32_t o3) {
+        const int32_t lo = j == 0 ? o0 : o1;
+        const int32_t hi = j == 2 ? o2 : o3;
+        return j < 2 ? lo : hi;
     }
 
-    // Each wave's loads of a stage fall in one 16-key quarter per (x) slot: a
-    // wave-wide K load covers 64 / SEGS consecutive keys and a V load one key
-    // octet, both inside one quarter. The quarter index is therefore uniform
-    // over the wave and is made scalar, so the source pick is a scalar select.
-    static_assert(64 % G::SEGS == 0 && 16 % (64 / G::SEGS) == 0, "wave-wide K load inside one quarter");
-    static_assert((D / 2) % 64 == 0 || 64 % (D / 2) == 0, "wave-wide V load inside one quarter");
+    static __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-    // FULL: every quarter of the stage lies inside the row (all but possibly
-    // the last stage), so no load needs a validity check.
-    template <bool FULL>
-    static __device__ __forceinline__ void load_stage(const uint16_t *kh, const uint16_t *vh,
-                                                      const Src src, int bk, Stage &st) {
-        const int t = threadIdx.x;
-        const int s0 = src.c0 < 0 ? -1 : src.c0 * bk + 16 * src.j0;
-        const int s1 = src.c1 < 0 ? -1 : src.c1 * bk + 16 * src.j1;
-        const int s2 = src.c2 < 0 ? -1 : src.c2 * bk + 16 * src.j2;
-        const int s3 = src.c3 < 0 ? -1 : src.c3 * bk + 16 * src.j3;
+    // Stage loads. K: wave-wide instruction X = KL w + x covers 16 keys of one
+    // tile and 4 segments (lane l: key l % 16, segment 4 (X % (SEGS / 4)) +
+    // l / 16), so in the segment-major LDS layout the 16 lanes of a quarter
+    // wave write 16 consecutive 16-byte slots. V: instruction X covers whole
+    // rows RPI X .. RPI X + RPI - 1 (lane l: row RPI X + l / SEGS, segment
+    // l % SEGS). Each instruction stays inside one 16-key tile, so the tile
+    // index follows from the wave index alone and the tile's offset is a
+    // scalar operand of the buffer load.
+    static __device__ __forceinline__ int k_tile(int w, int x) { return (KL * w + x) / (G::SEGS / 4); }
+    static __device__ __forceinline__ int k_segq(int w, int x) { return (KL * w + x) % (G::SEGS / 4); }
+    static __device__ __forceinline__ int v_row(int w, int x) { return RPI * (KL * w + x); }
+
+    struct LoadOffsets {
+        int32_t k[KL], v[KL];      // bytes inside a 16-key tile
+    };
+    static __device__ __forceinline__ LoadOffsets load_offsets() {
+        const int l = threadIdx.x & 63, w = wave_id();
+        LoadOffsets lo;
 #pragma unroll
         for (int x = 0; x < KL; ++x) {
-            const int idx = t + x * THREADS;
-            const int key = idx / G::SEGS, seg = idx % G::SEGS;
-            const int quarter = __builtin_amdgcn_readfirstlane(key / 16);
-            const int qs = key < KCH ? pick(quarter, s0, s1, s2, s3) : -1;
-            if (FULL || qs >= 0)
-                st.k[x] = *reinterpret_cast<const u32x4 *>(kh + int64_t(qs + key % 16) * D + seg * 8);
-            else
-                st.k[x] = u32x4{0u, 0u, 0u, 0u};
+            lo.k[x] = ((l % 16) * D + (4 * k_segq(w, x) + l / 16) * 8) * 2;
+            lo.v[x] = ((v_row(w, x) % 16 + l / G::SEGS) * D + (l % G::SEGS) * 8) * 2;
         }
-#pragma unroll
-        for (int x = 0; x < VL; ++x) {
-            const int task = t + x * THREADS;
-            const int oct = task / (D / 2), dp = task % (D / 2);
-            const int quarter = __builtin_amdgcn_readfirstlane(oct / 2);
-            const int qs = oct < KCH / 8 ? pick(quarter, s0, s1, s2, s3) : -1;
-            if (FULL || qs >= 0) {
-                const uint16_t *vp = vh + int64_t(qs + 8 * (oct & 1)) * D + 2 * dp;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) st.v[x][i] = *reinterpret_cast<const uint32_t *>(vp + int64_t(i) * D);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) st.v[x][i] = 0u;
-            }
-        }
+        return lo;
     }
 
-    static __device__ __forceinline__ void store_stage(char *stage, const Stage &st) {
-        const int t = threadIdx.x;
+    static __device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                                      const LoadOffsets &lo, const Src &src, int bk, Stage &st) {
+        const int w = wave_id();
+        __builtin_assume(w >= 0 && w < NW);
+        const int32_t o0 = __builtin_amdgcn_readfirstlane((src.c0 * bk + 16 * src.j0) * (D * 2));
+        const int32_t o1 = __builtin_amdgcn_readfirstlane((src.c1 * bk + 16 * src.j1) * (D * 2));
+        const int32_t o2 = __builtin_amdgcn_readfirstlane((src.c2 * bk + 16 * src.j2) * (D * 2));
+        const int32_t o3 = __builtin_amdgcn_readfirstlane((src.c3 * bk + 16 * src.j3) * (D * 2));
 #pragma unroll
         for (int x = 0; x < KL; ++x) {
-            const int idx = t + x * THREADS;
-            const int key = idx / G::SEGS, seg = idx % G::SEGS;
-            if (key < KCH) {
-                const int kk = key % 32;
-                char *kb = stage + (key / 32) * G::SUB_BYTES;
-                *reinterpret_cast<u32x4 *>(kb + (kk * G::SEGS + (seg ^ kswz<D>(kk))) * 16) = st.k[x];
-            }
-        }
-#pragma unroll
-        for (int x = 0; x < VL; ++x) {
-            const int task = t + x * THREADS;
-            const int oct = task / (D / 2), dp = task % (D / 2);
-            if (oct < KCH / 8) {
-                u32x4 lo, hi;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    lo[j] = __builtin_amdgcn_perm(st.v[x][2 * j + 1], st.v[x][2 * j], 0x05040100u);
-                    hi[j] = __builtin_amdgcn_perm(st.v[x][2 * j + 1], st.v[x][2 * j], 0x07060302u);
-                }
-                char *vt = stage + (oct / 4) * G::SUB_BYTES + G::SUB_K;
-                const int kg = oct % 4;
-                *reinterpret_cast<u32x4 *>(vt + (kg * D + 2 * dp) * 16) = lo;
-                *reinterpret_cast<u32x4 *>(vt + (kg * D + 2 * dp + 1) * 16) = hi;
-            }
+            st.k[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    krs, lo.k[x], pick(k_tile(w, x), o0, o1, o2, o3), 0));
+            st.v[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    vrs, lo.v[x], pick(v_row(w, x) / 16, o0, o1, o2, o3), 0));
         }
     }
 
-    // One 32-key sub-step for NG row groups. TAIL: only keys 0..15 are valid.
-    template <int NG, bool ONLINE, bool TAIL>
-    static __device__ __forceinline__ void compute_sub(const char *sub, const bf16x8 (&qf)[ar(NG)][G::DS],
-                                                       f32x4 (&acc)[ar(NG)][G::DT], f32x4 (&lsum)[ar(NG)],
-                                                       float (&mrow)[ar(NG)], const float (&brow)[ar(NG)], float c) {
+    struct StoreOffsets {
+        int32_t k[KL], v[KL];      // bytes inside an LDS stage
+    };
+    static __device__ __forceinline__ StoreOffsets store_offsets() {
+        const int l = threadIdx.x & 63, w = wave_id();
+        StoreOffsets so;
+#pragma unroll
+        for (int x = 0; x < KL; ++x) {
+            const int key = 16 * k_tile(w, x) + l % 16;
+            so.k[x] = (key / 32) * G::SUB_BYTES + ((4 * k_segq(w, x) + l / 16) * 32 + key % 32) * 16;
+            const int row = v_row(w, x) + l / G::SEGS;
+            so.v[x] = (row / 32) * G::SUB_BYTES + G::SUB_K + (row % 32) * G::VRS + (l % G::SEGS) * 16;
+        }
+        return so;
+    }
+
+    static __device__ __forceinline__ void store_stage(char *stage, const StoreOffsets &so, const Stage &st) {
+#pragma unroll
+        for (int x = 0; x < KL; ++x) {
+            *reinterpret_cast<u32x4 *>(stage + so.k[x]) = st.k[x];
+            *reinterpret_cast<u32x4 *>(stage + so.v[x]) = st.v[x];
+        }
+    }
+
+    // LDS byte offsets of this lane's fragment reads relative to a sub-step;
+    // the k-step / column tile adds an immediate.
+    //   K: lane (n, h) reads key sigma(n), segment 2 ks + h.
+    //   V: transposing reads, per 16-lane group four rows of 16 d: lane a of
+    //      the group addresses row a / 4 and d 4 (a % 4) of the group's block
+    //      and receives d = its own column, four consecutive keys.
+    struct ReadOffsets {
+        int32_t k, v;
+    };
+    static __device__ __forceinline__ ReadOffsets read_offsets() {
+        const int lane = threadIdx.x & 63;
+        const int n = lane & 31, h = lane >> 5;
+        const int a = lane & 15, n0 = 16 * ((lane >> 4) & 1);
+        ReadOffsets ro;
+        ro.k = (h * 32 + sigma(n)) * 16;
+        ro.v = G::SUB_K + (8 * h + a / 4) * G::VRS + (n0 + 4 * (a % 4)) * 2;
+        return ro;
+    }
+
+    // K fragments of one 32-key sub-step: lane (n, h) holds key sigma(n),
+    // d = 16 ks + 8 h .. + 8 for each k-step ks.
+    static __device__ __forceinline__ void read_k(const char *sub, const ReadOffsets &ro, bf16x8 (&ka)[G::KS]) {
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks) ka[ks] = *reinterpret_cast<const bf16x8 *>(sub + ro.k + ks * 1024);
+    }
+
+    // V^T fragments (A operand of p.v): lane (n, h) holds d = 32 dt + n and
+    // keys 16 ks + 8 h .. + 8, from two transposing reads of four keys each.
+    template <int PVK>
+    static __device__ __forceinline__ void read_v(const char *sub, const ReadOffsets &ro, bf16x8 (&va)[G::DT][2]) {
+#pragma unroll
+        for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+            for (int ks = 0; ks < PVK; ++ks) {
+                const char *vp = sub + ro.v + 16 * ks * G::VRS + 64 * dt;
+                const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vp));
+                const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vp + 4 * G::VRS));
+                va[dt][ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+    }
+
+    // S^T of one 32-key sub-step for this wavefront's 32 query rows.
+    static __device__ __forceinline__ f32x16 qk(const bf16x8 (&ka)[G::KS], const bf16x8 (&qf)[G::KS]) {
+        f32x16 s = {};
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s, 0, 0, 0);
+        return s;
+    }
+
+    // Row state of this wavefront's tile. Lane (n, h): query n, keys of half h.
+    struct Rows {
+        bf16x8 qf[G::KS];          // Q fragments (B operand of q.k)
+        f32x16 acc[G::DT];         // O^T accumulators, d = 32 dt + 8 (i / 4) + 4 h + i % 4
+        f32x16 s;                  // scores of the current sub-step
+        float lsum, mrow, brow;    // this lane's part of the row sum; running max; bound shift
+    };
+
+    // Softmax weights of a sub-step (bf16, the p.v B operands) and their
+    // contribution to this lane's row sum. PVK = 1: only keys 0..15 of the
+    // sub-step are valid.
+    template <bool ONLINE, int PVK>
+    static __device__ __forceinline__ void weights(Rows &rw, float c, bf16x8 (&pk)[2]) {
+        constexpr int NV = 8 * PVK;
+        float pr[16];
+        if constexpr (!ONLINE) {
+            // bound path: p = exp2(s c - B_i log2 e), no max, no rescale
+#pragma unroll
+            for (int i = 0; i < NV; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(rw.s[i], c, -rw.brow));
+        } else {
+            // online fallback: running max over the row (both halves), rescale
+            float t[16];
+#pragma unroll
+            for (int i = 0; i < NV; ++i) t[i] = rw.s[i] * c;
+            float cm = t[0];
+#pragma unroll
+            for (int i = 1; i < NV; ++i) cm = fmaxf(cm, t[i]);
+            const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(cm), __float_as_uint(cm), false, false);
+            cm = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
+            const float mn = fmaxf(rw.mrow, cm);
+            const float alpha = __builtin_amdgcn_exp2f(rw.mrow - mn);
+            rw.mrow = mn;
+            rw.lsum *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < G::DT; ++dt) rw.acc[dt] *= alpha;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) pr[i] = __builtin_amdgcn_exp2f(t[i] - mn);
+        }
+#pragma unroll
+        for (int ks = 0; ks < PVK; ++ks)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pk[ks][i] = static_cast<__bf16>(pr[8 * ks + i]);
+        // row sums of the bf16 weights actually used in p.v
+        const bf16x2 ones2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+#pragma unroll
+        for (int ks = 0; ks < PVK; ++ks) {
+            rw.lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[ks], pk[ks], 0, 1), ones2, rw.lsum, false);
+            rw.lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[ks], pk[ks], 2, 3), ones2, rw.lsum, false);
+            rw.lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[ks], pk[ks], 4, 5), ones2, rw.lsum, false);
+            rw.lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[ks], pk[ks], 6, 7), ones2, rw.lsum, false);
+        }
+    }
+
+    // One software-pipelined sub-step: weights of the current sub-step (its
+    // scores were computed one step earlier), the next sub-step's scores
+    // (NEXT) and the current sub-step's p.v. HALF: only keys 0..15 of the
+    // current sub-step are valid (the row's last, odd 16-key tile).
+    template <int NG, bool ONLINE, bool HALF, bool NEXT>
+    static __device__ __forceinline__ void step(const char *cur, const char *nxt, const ReadOffsets &ro, Rows &rw,
+                                                float c) {
         if constexpr (NG > 0) {
-            const int lane = threadIdx.x & 63;
-            const int m = lane & 15, g = lane >> 4;
-            bf16x8 ka[2][G::DS];
+            constexpr int PVK = HALF ? 1 : 2;
+            bf16x8 va[G::DT][2];
+            bf16x8 ka[G::KS];
+            if constexpr (NEXT) read_k(nxt, ro, ka);
+            read_v<PVK>(cur, ro, va);
+            bf16x8 pk[2];
+            weights<ONLINE, PVK>(rw, c, pk);
+            if constexpr (NEXT) rw.s = qk(ka, rw.qf);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int r = 8 * (m >> 2) + 4 * j + (m & 3);
-#pragma unroll
-                for (int ds = 0; ds < G::DS; ++ds) {
-                    const int seg = 4 * ds + g;
-                    ka[j][ds] = *reinterpret_cast<const bf16x8 *>(sub + (r * G::SEGS + (seg ^ kswz<D>(r))) * 16);
-                }
-            }
-            bf16x8 va[G::DT];
-            const char *vt = sub + G::SUB_K;
-#pragma unroll
-            for (int dt = 0; dt < G::DT; ++dt)
-                va[dt] = *reinterpret_cast<const bf16x8 *>(vt + (g * D + 16 * dt + m) * 16);
-            bf16x8 ones8;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ones8[i] = static_cast<__bf16>(1.0f);
-
-#pragma unroll
-            for (int rg = 0; rg < NG; ++rg) {
-                f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ds = 0; ds < G::DS; ++ds) {
-                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][ds], qf[rg][ds], s0, 0, 0, 0);
-                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][ds], qf[rg][ds], s1, 0, 0, 0);
-                }
-                // this lane: query row m of the group, keys 8g .. 8g+7 of the sub-step
-                const float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-                float pr[8];
-                if constexpr (!ONLINE) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(x[i], c, -brow[rg]));
-                    if constexpr (TAIL) {
-                        if (g >= 2) {
-#pragma unroll
-                            for (int i = 0; i < 8; ++i) pr[i] = 0.0f;
-                        }
-                    }
-                } else {
-                    float t[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) t[i] = x[i] * c;
-                    if constexpr (TAIL) {
-                        if (g >= 2) {
-#pragma unroll
-                            for (int i = 0; i < 8; ++i) t[i] = -__builtin_huge_valf();
-                        }
-                    }
-                    float cm = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])),
-                                     fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
-                    cm = fmaxf(cm, __shfl_xor(cm, 16));
-                    cm = fmaxf(cm, __shfl_xor(cm, 32));
-                    const float mn = fmaxf(mrow[rg], cm);
-                    const float alpha = __builtin_amdgcn_exp2f(mrow[rg] - mn);
-                    mrow[rg] = mn;
-                    lsum[rg] *= alpha;
-#pragma unroll
-                    for (int dt = 0; dt < G::DT; ++dt) acc[rg][dt] *= alpha;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(t[i] - mn);
-                }
-                bf16x8 pk;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) pk[i] = static_cast<__bf16>(pr[i]);
-                // row sums of the bf16 weights actually used in p.v, on the matrix
-                // unit: a ones "V^T" tile gives every output row the sum over keys
-                lsum[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pk, lsum[rg], 0, 0, 0);
+            for (int ks = 0; ks < PVK; ++ks)
 #pragma unroll
                 for (int dt = 0; dt < G::DT; ++dt)
-                    acc[rg][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pk, acc[rg][dt], 0, 0, 0);
-            }
+                    rw.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][ks], pk[ks], rw.acc[dt], 0, 0, 0);
         }
     }
 
-    template <int NG, bool ONLINE>
-    static __device__ __forceinline__ void compute_stage(const char *stage, int valid_quarters,
-                                                         const bf16x8 (&qf)[ar(NG)][G::DS], f32x4 (&acc)[ar(NG)][G::DT],
-                                                         f32x4 (&lsum)[ar(NG)], float (&mrow)[ar(NG)],
-                                                         const float (&brow)[ar(NG)], float c) {
-        if (valid_quarters >= G::QUARTERS) {
-#pragma unroll
-            for (int sb = 0; sb < G::SUB; ++sb)
-                compute_sub<NG, ONLINE, false>(stage + sb * G::SUB_BYTES, qf, acc, lsum, mrow, brow, c);
-        } else {
-#pragma unroll
-            for (int sb = 0; sb < G::SUB; ++sb) {
-                const int vq = valid_quarters - 2 * sb;
-                if (vq >= 2)
-                    compute_sub<NG, ONLINE, false>(stage + sb * G::SUB_BYTES, qf, acc, lsum, mrow, brow, c);
-                else if (vq == 1)
-                    compute_sub<NG, ONLINE, true>(stage + sb * G::SUB_BYTES, qf, acc, lsum, mrow, brow, c);
-            }
-        }
-    }
-
-    // The block-list walk: stages of KCH keys, double-buffered in LDS, the next
-    // stage's global loads in flight while the current one is computed.
+    // The block-list walk in stages of 64 keys. Stage s sits in LDS buffer
+    // s % 3; while stage s is computed, stage s + 1 is already in LDS (the
+    // scores of the next sub-step are computed ahead), stage s + 2 is stored
+    // from registers and stage s + 3 is in flight from global memory. One
+    // barrier per stage. NG = 0: a wavefront without rows still stages K/V
+    // and meets every barrier.
     template <int NG, bool ONLINE>
     static __device__ __forceinline__ void walk(const AttnParams &p, char *smem, const uint16_t *kh,
                                                 const uint16_t *vh, int32_t e0, int32_t e1, int32_t nquart,
-                                                const bf16x8 (&qf)[ar(NG)][G::DS], f32x4 (&acc)[ar(NG)][G::DT],
-                                                f32x4 (&lsum)[ar(NG)], float (&mrow)[ar(NG)], const float (&brow)[ar(NG)]) {
-        const int nst = (nquart + G::QUARTERS - 1) / G::QUARTERS;
+                                                Rows &rw) {
+        const int nst = (nquart + 3) / 4;
+        if (nst == 0) return;                       // (a plan row always lists its own frame)
         const int hpb = p.block_k / 16;
         const cint32 *col = (const cint32 *)(p.col_idx);
+        const int64_t slab = int64_t(p.seq_len) * D * 2;
+        const __amdgpu_buffer_rsrc_t krs = head_rsrc(kh, slab), vrs = head_rsrc(vh, slab);
+        const LoadOffsets lo = load_offsets();
+        const StoreOffsets so = store_offsets();
+        const ReadOffsets ro = read_offsets();
         Cursor cur{e0, 0};
         Stage st;
-        const bool last_full = nquart % G::QUARTERS == 0;
-        auto load = [&](int stage_idx, const Src &src) {
-            if (stage_idx < nst - 1 || last_full)
-                load_stage<true>(kh, vh, src, p.block_k, st);
-            else
-                load_stage<false>(kh, vh, src, p.block_k, st);
-        };
-        if (nst > 0) {
-            load(0, next_src(col, cur, e1, hpb));
-            store_stage(smem, st);
-        }
-        if (nst > 1) load(1, next_src(col, cur, e1, hpb));
-        Src nxt = next_src(col, cur, e1, hpb);           // stage 2, fetched a stage early
+        char *const b0 = smem, *const b1 = smem + G::STAGE, *const b2 = smem + 2 * G::STAGE;
+
+        load_stage(krs, vrs, lo, next_src(col, cur, e1, hpb), p.block_k, st);
+        store_stage(b0, so, st);
+        load_stage(krs, vrs, lo, next_src(col, cur, e1, hpb), p.block_k, st);
+        store_stage(b1, so, st);
+        load_stage(krs, vrs, lo, next_src(col, cur, e1, hpb), p.block_k, st);
+        Src nxt = next_src(col, cur, e1, hpb);
         lds_barrier();
-        for (int s = 0; s < nst - 1; ++s) {
-            store_stage(smem + ((s + 1) & 1) * G::STAGE, st);
-            if (s + 2 < nst) {
-                load(s + 2, nxt);
-                nxt = next_src(col, cur, e1, hpb);
-            }
-            compute_stage<NG, ONLINE>(smem + (s & 1) * G::STAGE, G::QUARTERS, qf, acc, lsum, mrow, brow, p.c);
-            lds_barrier();
+        if constexpr (NG > 0) {
+            bf16x8 ka[G::KS];
+            read_k(b0, ro, ka);
+            rw.s = qk(ka, rw.qf);
         }
-        if (nst > 0)
-            compute_stage<NG, ONLINE>(smem + ((nst - 1) & 1) * G::STAGE, nquart - (nst - 1) * G::QUARTERS,
-                                      qf, acc, lsum, mrow, brow, p.c);
+
+        // Every stage but the last: two full sub-steps, each with a next one.
+        // The loop is unrolled by three so that every LDS address is a fixed
+        // per-lane offset plus an immediate.
+        auto body = [&](char *bc, char *bn, char *bs) {
+            store_stage(bs, so, st);
+            load_stage(krs, vrs, lo, nxt, p.block_k, st);
+            nxt = next_src(col, cur, e1, hpb);
+            step<NG, ONLINE, false, true>(bc, bc + G::SUB_BYTES, ro, rw, p.c);
+            step<NG, ONLINE, false, true>(bc + G::SUB_BYTES, bn, ro, rw, p.c);
+            lds_barrier();
+        };
+        int s = 0;
+        for (; s + 3 <= nst - 1; s += 3) {
+            body(b0, b1, b2);
+            body(b1, b2, b0);
+            body(b2, b0, b1);
+        }
+        if (s < nst - 1) {
+            body(b0, b1, b2);
+            ++s;
+            if (s < nst - 1) {
+                body(b1, b2, b0);
+                ++s;
+            }
+        }
+        // the last stage: 1 to 4 valid 16-key tiles
+        const int r3 = (nst - 1) % 3;
+        char *const b = r3 == 0 ? b0 : (r3 == 1 ? b1 : b2);
+        switch (nquart - 4 * (nst - 1)) {
+            case 1: step<NG, ONLINE, true, false>(b, b, ro, rw, p.c); break;
+            case 2: step<NG, ONLINE, false, false>(b, b, ro, rw, p.c); break;
+            case 3:
+                step<NG, ONLINE, false, true>(b, b + G::SUB_BYTES, ro, rw, p.c);
+                step<NG, ONLINE, true, false>(b + G::SUB_BYTES, b, ro, rw, p.c);
+                break;
+            default:
+                step<NG, ONLINE, false, true>(b, b + G::SUB_BYTES, ro, rw, p.c);
+                step<NG, ONLINE, false, false>(b + G::SUB_BYTES, b, ro, rw, p.c);
+                break;
+        }
     }
 
-    // NG valid row groups for this wavefront, starting at group my_g0 of the query block.
+    // This wavefront's tile: rows row0 .. row0 + nvalid - 1 (nvalid 16 or 32)
+    // for NG = 1; NG = 0 stages K/V with the others and meets every barrier.
     template <int NG>
-    static __device__ __forceinline__ void tile(const AttnParams &p, char *smem, int64_t head_row0,
-                                                int32_t qb, int my_g0, const uint16_t *kh,
-                                                const uint16_t *vh, int32_t e0, int32_t e1, int32_t nquart,
-                                                bool online, float mk) {
+    static __device__ __forceinline__ void tile(const AttnParams &p, char *smem, int64_t head_row0, int32_t row0,
+                                                int nvalid, const uint16_t *kh, const uint16_t *vh, int32_t e0,
+                                                int32_t e1, int32_t nquart, bool online, float mk) {
         const int lane = threadIdx.x & 63;
-        const int m = lane & 15, g = lane >> 4;
-        // a wavefront without rows (NG == 0) still stages K/V and meets every barrier
-        int rows[ar(NG)];
-        bf16x8 qf[ar(NG)][G::DS];
-        f32x4 acc[ar(NG)][G::DT];
-        f32x4 lsum[ar(NG)];            // row sums (all four entries equal; see compute_sub)
-        float mrow[ar(NG)], brow[ar(NG)];
+        const int n = lane & 31, h = lane >> 5;
+        const int32_t row = row0 + (n < nvalid ? n : nvalid - 1);   // rows past the tile recompute a valid one
+        Rows rw;
+        rw.lsum = 0.0f;
+        rw.mrow = -__builtin_huge_valf();
+        rw.brow = 0.0f;
+        if constexpr (NG > 0) {
+            const uint16_t *qr = p.q + (head_row0 + row) * D;
 #pragma unroll
-        for (int rg = 0; rg < NG; ++rg) {
-            rows[rg] = qb * p.block_q + (my_g0 + rg) * 16 + m;
-            const uint16_t *qr = p.q + (head_row0 + rows[rg]) * D;
+            for (int ks = 0; ks < G::KS; ++ks) rw.qf[ks] = *reinterpret_cast<const bf16x8 *>(qr + 16 * ks + 8 * h);
 #pragma unroll
-            for (int ds = 0; ds < G::DS; ++ds)
-                qf[rg][ds] = *reinterpret_cast<const bf16x8 *>(qr + 32 * ds + 8 * g);
-#pragma unroll
-            for (int dt = 0; dt < G::DT; ++dt) acc[rg][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            lsum[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
-            mrow[rg] = -__builtin_huge_valf();
-            brow[rg] = online ? 0.0f : p.c * p.qnorm[head_row0 + rows[rg]] * mk;
+            for (int dt = 0; dt < G::DT; ++dt) rw.acc[dt] = f32x16{};
+            if (!online) rw.brow = p.c * p.qnorm[head_row0 + row] * mk;
         }
         if (online)
-            walk<NG, true>(p, smem, kh, vh, e0, e1, nquart, qf, acc, lsum, mrow, brow);
+            walk<NG, true>(p, smem, kh, vh, e0, e1, nquart, rw);
         else
-            walk<NG, false>(p, smem, kh, vh, e0, e1, nquart, qf, acc, lsum, mrow, brow);
+            walk<NG, false>(p, smem, kh, vh, e0, e1, nquart, rw);
         if constexpr (NG > 0) {
-            // epilogue: normalise by the row sum, bf16, store
+            // both halves of a row hold partial sums over disjoint keys
+            const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(rw.lsum), __float_as_uint(rw.lsum),
+                                                              false, false);
+            const float inv = 1.0f / (__uint_as_float(sw2[0]) + __uint_as_float(sw2[1]));
+            if (n < nvalid) {
+                uint16_t *orow = p.o + (head_row0 + row) * D;
 #pragma unroll
-            for (int rg = 0; rg < NG; ++rg) {
-                const float inv = 1.0f / lsum[rg][0];
-                uint16_t *orow = p.o + (head_row0 + rows[rg]) * D;
+                for (int dt = 0; dt < G::DT; ++dt)
 #pragma unroll
-                for (int dt = 0; dt < G::DT; ++dt) {
-                    __bf16 h4[4];
+                    for (int a = 0; a < 4; ++a) {
+                        __bf16 h4[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) h4[i] = static_cast<__bf16>(acc[rg][dt][i] * inv);
-                    uint2 w;
-                    w.x = uint32_t(__builtin_bit_cast(uint16_t, h4[0])) |
-                          (uint32_t(__builtin_bit_cast(uint16_t, h4[1])) << 16);
-                    w.y = uint32_t(__builtin_bit_cast(uint16_t, h4[2])) |
-                          (uint32_t(__builtin_bit_cast(uint16_t, h4[3])) << 16);
-                    *reinterpret_cast<uint2 *>(orow + 16 * dt + 4 * g) = w;
-                }
+                        for (int i = 0; i < 4; ++i) h4[i] = static_cast<__bf16>(rw.acc[dt][4 * a + i] * inv);
+                        uint2 w;
+                        w.x = uint32_t(__builtin_bit_cast(uint16_t, h4[0])) |
+                              (uint32_t(__builtin_bit_cast(uint16_t, h4[1])) << 16);
+                        w.y = uint32_t(__builtin_bit_cast(uint16_t, h4[2])) |
+                              (uint32_t(__builtin_bit_cast(uint16_t, h4[3])) << 16);
+                        *reinterpret_cast<uint2 *>(orow + 32 * dt + 8 * a + 4 * h) = w;
+                    }
             }
-        }
-    }
-
-    template <int NG>
-    static __device__ __forceinline__ void dispatch(int ng, const AttnParams &p, char *smem, int64_t head_row0,
-                                                    int32_t qb, int my_g0, const uint16_t *kh,
-                                                    const uint16_t *vh, int32_t e0, int32_t e1, int32_t nquart,
-                                                    bool online, float mk) {
-        if constexpr (NG >= 0) {
-            if (ng == NG)
-                tile<NG>(p, smem, head_row0, qb, my_g0, kh, vh, e0, e1, nquart, online, mk);
-            else
-                dispatch<NG - 1>(ng, p, smem, head_row0, qb, my_g0, kh, vh, e0, e1, nquart, online, mk);
         }
     }
 
     static __device__ void run(const AttnParams &p) {
         extern __shared__ __attribute__((aligned(16))) char smem[];
-        float *red = reinterpret_cast<float *>(smem + 2 * G::STAGE);
+        float *red = reinterpret_cast<float *>(smem + 2 * G::STAGE);   // stage buffer 2 is free until the walk
         const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
         // XCD-aware order: consecutive workgroup ids go to different XCDs, so
@@ -681,9 +709,10 @@ struct AttnKernel {
         const int64_t head_row0 = hb * p.seq_len;
         const uint16_t *kh = p.k + head_row0 * D;
         const uint16_t *vh = p.v + head_row0 * D;
-        const int32_t e0 = p.row_ptr[qb], e1 = p.row_ptr[qb + 1];
+        const int32_t e0 = __builtin_amdgcn_readfirstlane(p.row_ptr[qb]);
+        const int32_t e1 = __builtin_amdgcn_readfirstlane(p.row_ptr[qb + 1]);
         const int32_t nquart = (e1 - e0) * (p.block_k / 16);
-        const bool online = p.eligible[hb] == 0;
+        const bool online = __builtin_amdgcn_readfirstlane(p.eligible[hb]) == 0;
 
         // bound path: largest key norm over the row's active key blocks
         float mk = 0.0f;
@@ -697,23 +726,26 @@ struct AttnKernel {
             for (int w = 0; w < NW; ++w) mk = fmaxf(mk, red[w]);
         }
 
-        const int groups = p.block_q / 16;
-        for (int sub = 0; sub < groups; sub += NW * RG) {
-            // spread the sub-tile's groups over the wavefronts, RG at most each
-            const int gsub = groups - sub < NW * RG ? groups - sub : NW * RG;
-            const int base = gsub / NW, extra = gsub % NW;
-            const int ng = base + (wave < extra ? 1 : 0);
-            const int my_g0 = sub + wave * base + (wave < extra ? wave : extra);
-            dispatch<RG>(ng, p, smem, head_row0, qb, my_g0, kh, vh, e0, e1, nquart, online, mk);
-            if (sub + NW * RG < groups) lds_barrier();     // LDS reused by the next sub-tile
+        // 32-row tiles of the query block (the last may hold 16 rows), one per
+        // wavefront, NW per pass over the keys
+        const int ntiles = (p.block_q + 31) / 32;
+        for (int t0 = 0; t0 < ntiles; t0 += NW) {
+            const int my = t0 + wave;
+            const int32_t row0 = qb * p.block_q + 32 * my;
+            const int nvalid = p.block_q - 32 * my < 32 ? p.block_q - 32 * my : 32;
+            if (my < ntiles)
+                tile<1>(p, smem, head_row0, row0, nvalid, kh, vh, e0, e1, nquart, online, mk);
+            else
+                tile<0>(p, smem, head_row0, row0, nvalid, kh, vh, e0, e1, nquart, online, mk);
+            if (t0 + NW < ntiles) lds_barrier();     // LDS reused by the next pass
         }
     }
 };
 
-template <int D, int RG, int NW, int KCH, int WPE>
-__global__ void __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(WPE, WPE)))
+template <int D>
+__global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 attention_kernel(AttnParams p) {
-    AttnKernel<D, RG, NW, KCH>::run(p);
+    AttnKernel<D>::run(p);
 }
 
 }  // namespace
@@ -772,21 +804,28 @@ int launch_bounds(const BoundsLaunch &a) {
     return err == hipSuccess ? 0 : int(err);
 }
 
-// Kernel configuration: 16-row groups per wavefront, wavefronts per workgroup,
-// keys per LDS stage, wavefronts per SIMD.
-template <int D, int RG, int NW, int KCH, int WPE>
+// One launch: 8 * ceil(work / 8) workgroups of 512 threads (the kernel remaps
+// ids XCD-first and returns for ids past the work), dynamic LDS for the three
+// stage buffers. The LDS size needs the function attribute, set once per
+// device.
+template <int D>
 int launch_cfg(const AttnParams &p, hipStream_t stream) {
-    using K = AttnKernel<D, RG, NW, KCH>;
-    auto fn = attention_kernel<D, RG, NW, KCH, WPE>;
-    static bool attr_done = false;
-    if (!attr_done) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, K::LDS_BYTES);
-        attr_done = true;
+    using K = AttnKernel<D>;
+    auto fn = attention_kernel<D>;
+    static std::atomic<uint64_t> attr_done{0};     // one bit per device
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return int(err);
+    const uint64_t bit = dev < 64 ? (uint64_t(1) << dev) : 0;
+    if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  K::LDS_BYTES);
+        if (err != hipSuccess) return int(err);
+        attr_done.fetch_or(bit, std::memory_order_acq_rel);
     }
     const unsigned grid = unsigned(p.per_xcd * 8);
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * NW), K::LDS_BYTES, stream, p);
-    const hipError_t err = hipGetLastError();
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(K::THREADS), K::LDS_BYTES, stream, p);
+    err = hipGetLastError();
     return err == hipSuccess ? 0 : int(err);
 }
 
@@ -816,8 +855,8 @@ int launch_attention(const AttentionLaunch &a) {
     p.n_kb = pl.n_kblocks;
     p.c = a.scale * kLog2e;
     hipStream_t stream = static_cast<hipStream_t>(a.stream);
-    if (a.head_dim == 128) return launch_cfg<128, FSA_RG, FSA_NW, FSA_KCH, FSA_WPE>(p, stream);
-    return launch_cfg<64, FSA_RG, FSA_NW, FSA_KCH, FSA_WPE>(p, stream);
+    if (a.head_dim == 128) return launch_cfg<128>(p, stream);
+    return launch_cfg<64>(p, stream);
 }
 
 }  // namespace fsa
