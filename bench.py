@@ -5,8 +5,10 @@
 One step is one pass of every stage of the path over one batch of synthetic
 input already resident in HBM: the host plan (fsa_plan into pinned memory and
 an async copy of its CSR to the device), fsa_bounds (norm array and per-head
-eligibility) and fsa_attention. W untimed steps, then K timed steps between two
-device synchronisations. Prints ONE JSON line:
+eligibility) and fsa_attention. Consecutive steps rotate over three copies of
+q, k, v (more than the 256 MB last-level cache holds at the 720p and 1080p
+shapes), so the bounds pass reads from HBM. W untimed steps, then K timed steps
+between two device synchronisations. Prints ONE JSON line:
 
 * value = active-block FLOPs (4 D per visible query/key pair) x K / time of the
   K steps, in TFLOP/s, and pct_of_peak against the bf16 dense MFMA peak;
@@ -65,6 +67,8 @@ def parse():
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
     ap.add_argument("--cpu-heads", type=int, default=4,
                     help="heads of the workload the CPU oracle is timed on")
+    ap.add_argument("--copies", type=int, default=3,
+                    help="copies of q, k, v that consecutive steps rotate over")
     return ap.parse_args()
 
 
@@ -119,7 +123,8 @@ def main():
     qc, kc, vc = synthetic.make_inputs(wl)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    q, k, v = (x.to(dev) for x in (qc, kc, vc))
+    inputs = [tuple(x.to(dev) for x in (qc, kc, vc)) for _ in range(max(1, args.copies))]
+    q = inputs[0][0]
     o = torch.empty_like(q)
 
     # plan: computed on the host every step into pinned memory, copied async
@@ -139,6 +144,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
+        q, k, v = inputs[i % len(inputs)]
         slot = i & 1
         if copied[slot] is not None:
             copied[slot].synchronize()                  # pinned buffer free again
@@ -218,13 +224,16 @@ def main():
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic("fsa_attention", wl.name),
             "mean_ms": round(attn_mean, 5),
+            "median_ms": round(float(np.median(attn_ms)), 5),
             "p10_ms": round(float(np.percentile(attn_ms, 10)), 5),
             "p90_ms": round(float(np.percentile(attn_ms, 90)), 5),
         },
         "bounds": {
             "kernels": "fsa_bounds (norms + bound reduce)",
             "mean_ms": round(float(bnd_ms.mean()), 5),
+            "median_ms": round(float(np.median(bnd_ms)), 5),
             "gbps": round(bounds_bytes / (float(bnd_ms.mean()) * 1e-3) / 1e9, 1),
+            "input_copies": len(inputs),
             "peak_gbps": PEAK_HBM_GBPS,
             "algorithmic_bytes": bounds_bytes,
             "traffic": measured_traffic("fsa_bounds_norms", wl.name),
