@@ -38,7 +38,10 @@ Readings where the pages are silent (each is restated where it is used):
   that is <= 256, ``bk`` the largest that is <= 128;
 * the row bound is taken over the row's active key blocks (a tighter valid
   bound than the global largest key norm), and a head is eligible for the bound
-  path iff its largest row bound is <= ``bound_limit`` (default 32).
+  path iff its largest row bound is <= ``bound_limit`` (default 32);
+* key mean-centring (optional): the mean is over all N keys of a head; the
+  row's exponent is shifted by scale q_i.mean plus the centred bound, and
+  eligibility checks the centred bound.
 
 Pins (``tests/test_oracle.py``): brute force with Python loops on tiny inputs,
 weight rows summing to one with exact zeros off the mask, the full window
@@ -46,7 +49,10 @@ reproducing ``torch``'s fp64 scaled-dot-product attention, the bound-shift
 softmax equal to max-subtract (mpmath at 50 digits and fp64), closed forms
 (q = 0, constant v, frame-indicator v), Cauchy-Schwarz on every active pair,
 the plan's closed-form block count and a hand-derived plan under
-``tests/golden/``, and key-permutation / head-independence invariances.
+``tests/golden/``, key-permutation / head-independence invariances, and for
+centring: keys built as an offset plus +/- pairs of known length (so the mean
+and the centred norms are known by construction), translation invariance of
+the centred bound, and the shift bounding every active score.
 """
 from __future__ import annotations
 
@@ -293,7 +299,7 @@ def effective_bound_limit(bound_limit: float) -> float:
 
 def bounds(q, k, frames: int, tokens_per_frame: int, window: int, ref_frame: int,
            scale: float, block_q: int = 0, block_k: int = 0,
-           bound_limit: float = DEFAULT_BOUND_LIMIT):
+           bound_limit: float = DEFAULT_BOUND_LIMIT, center: bool = False):
     """Norm array and per-head eligibility, fp64.
 
     qnorm[b,h,i] = ||q_i||_2; kmax[b,h,kb] = max over the block's keys of ||k_j||_2;
@@ -301,14 +307,32 @@ def bounds(q, k, frames: int, tokens_per_frame: int, window: int, ref_frame: int
     the query block holding i (Cauchy-Schwarz: s_ij <= B_i on every active pair);
     bmax[b,h] = max_i B_i; eligible[b,h] = bmax <= bound_limit.
 
-    Returns dict(qnorm, kmax, row_bound, bmax, eligible, info).
+    With ``center`` the keys are mean-centred first [vi:Softmax]: the pages
+    note that keys share a large common component, that removing the mean key
+    tightens the bound, and that the softmax does not change. Reading: the mean
+    is taken over all N keys of the (b, h) head, kmean[b,h] = (1/N) sum_j k_j,
+    and kmax becomes max ||k_j - kmean|| per key block. Since
+    s_ij = scale q_i.kmean + scale q_i.(k_j - kmean), the per-row shift
+    C_i = scale q_i.kmean + B_i bounds s_ij on every active pair, while
+    s_ij - C_i stays >= -2 B_i; B_i (the centred bound) is what eligibility
+    checks. The term scale q_i.kmean is the same for every key of row i, so
+    the softmax is unchanged. Without ``center`` kmean is zero and C_i = B_i.
+
+    Returns dict(qnorm, kmax, kmean, row_bound, row_shift, bmax, eligible, info):
+    row_bound is B_i, row_shift is C_i (the value each row's exponent is
+    shifted by on the bound path).
     """
     q, k = _f64(q), _f64(k)
     info, row_ptr, col_idx = plan(frames, tokens_per_frame, window, ref_frame, block_q, block_k)
     bq, bk = info["block_q"], info["block_k"]
     n_qb, n_kb = info["n_qblocks"], info["n_kblocks"]
+    if center:
+        kmean = k.mean(axis=2)                                   # [B, H, D]
+    else:
+        kmean = np.zeros(k.shape[:2] + k.shape[3:])
+    kc = k - kmean[:, :, None, :]
     qnorm = np.sqrt((q * q).sum(axis=-1))
-    knorm = np.sqrt((k * k).sum(axis=-1))
+    knorm = np.sqrt((kc * kc).sum(axis=-1))
     bsz, heads, n = qnorm.shape
     kmax = knorm.reshape(bsz, heads, n_kb, bk).max(axis=-1)
     row_bound = np.empty_like(qnorm)
@@ -317,10 +341,11 @@ def bounds(q, k, frames: int, tokens_per_frame: int, window: int, ref_frame: int
         mk = kmax[:, :, kbs].max(axis=-1)                         # [B, H]
         sl = slice(qb * bq, (qb + 1) * bq)
         row_bound[:, :, sl] = scale * qnorm[:, :, sl] * mk[:, :, None]
+    row_shift = row_bound + scale * (q @ kmean[:, :, :, None])[..., 0]
     bmax = row_bound.max(axis=-1)
     eligible = (bmax <= effective_bound_limit(bound_limit)).astype(np.int32)
-    return dict(qnorm=qnorm, kmax=kmax, row_bound=row_bound, bmax=bmax,
-                eligible=eligible, info=info)
+    return dict(qnorm=qnorm, kmax=kmax, kmean=kmean, row_bound=row_bound, row_shift=row_shift,
+                bmax=bmax, eligible=eligible, info=info)
 
 
 def row_bound_by_frames(q, k, frames: int, tokens_per_frame: int, window: int,

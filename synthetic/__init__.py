@@ -17,6 +17,9 @@ are not available:
 * ``sr1080``        1 x 8 x 46,800 (13 x 3600, a 45x80 latent), D=128, +-2
 * ``bound_stress``  the ``sr720`` shape with heavy-tailed q/k row norms
 * ``dense``         1 x 8 x 16,800 (14 x 1200), D=128, window covers all frames
+* ``key_offset``    the ``sr720`` shape with a large offset shared by all keys
+                    of a head (the "common component" that key centring removes,
+                    article section on freeing the softmax)
 
 All use reference frame 0 and scale 1/sqrt(D) rounded to fp32.
 """
@@ -60,6 +63,7 @@ WORKLOADS = {
     "sr1080": Workload("sr1080", 1, 8, 128, 13, 3600, 2, 0),
     "bound_stress": Workload("bound_stress", 1, 8, 128, 21, 1200, 1, 0, dist="bound_stress"),
     "dense": Workload("dense", 1, 8, 128, 14, 1200, 13, 0),
+    "key_offset": Workload("key_offset", 1, 8, 128, 21, 1200, 1, 0, dist="key_offset"),
 }
 
 # Heavy-tailed inputs for ``bound_stress``: q and k rows are multiplied by
@@ -68,6 +72,10 @@ WORKLOADS = {
 STRESS_SIGMA = 1.0
 STRESS_KEY_FRACTION = 0.05
 STRESS_KEY_FACTOR = 8.0
+
+# ``key_offset``: per (b, h) one direction u ~ N(0, I_D), scaled to this length,
+# is added to every key row of the head.
+KEY_OFFSET_NORM = 40.0
 
 
 def make_inputs(wl: Workload, device: str = "cpu"):
@@ -78,7 +86,9 @@ def make_inputs(wl: Workload, device: str = "cpu"):
     ``bound_stress`` the same generator continues after v with the q row
     factors, the k row factors, and per (b, h) one ``randperm`` whose first
     round(0.05 N) entries pick the key rows that are scaled x8; the rounding to
-    bf16 happens after all scaling.
+    bf16 happens after all scaling. For ``key_offset`` the generator continues
+    after v with one offset direction per (b, h), added to that head's keys
+    before the rounding.
     """
     g = torch.Generator("cpu").manual_seed(wl.seed)
     shape = (wl.batch, wl.heads, wl.seq_len, wl.head_dim)
@@ -95,6 +105,9 @@ def make_inputs(wl: Workload, device: str = "cpu"):
             for h in range(wl.heads):
                 idx = torch.randperm(wl.seq_len, generator=g)[:n_big]
                 k[b, h, idx] *= STRESS_KEY_FACTOR
+    elif wl.dist == "key_offset":
+        u = torch.randn((wl.batch, wl.heads, 1, wl.head_dim), generator=g, dtype=torch.float32)
+        k += u * (KEY_OFFSET_NORM / u.norm(dim=-1, keepdim=True))
     elif wl.dist != "normal":
         raise ValueError(f"unknown distribution {wl.dist!r}")
     out = [t.to(torch.bfloat16) for t in (q, k, v)]

@@ -317,8 +317,70 @@ def check_invariances(orc):
     assert np.abs(o - o0).max() > 1e-6
 
 
+def check_centering(orc):
+    """Key mean-centring [vi:Softmax] on keys whose mean and centred lengths are
+    known by construction: a shared offset mu0 of length 40 plus deviations
+    +dev_j (first half of the keys) and -dev_j (second half), so the mean is
+    exactly mu0 and ||k_j - mu0|| is the drawn length. The pairs straddle every
+    block, so a per-block mean would differ from mu0."""
+    frames, t, d, w, r = 4, 32, 8, 1, 2
+    n = frames * t
+    scale = 0.3
+    rng = np.random.default_rng(5)
+    mu0 = rng.standard_normal((1, 2, d))
+    mu0 *= 40.0 / np.linalg.norm(mu0, axis=-1, keepdims=True)
+    u = rng.standard_normal((1, 2, n // 2, d))
+    u /= np.linalg.norm(u, axis=-1, keepdims=True)
+    length = rng.uniform(0.5, 2.0, (1, 2, n // 2))
+    dev = u * length[..., None]
+    k = mu0[:, :, None, :] + np.concatenate([dev, -dev], axis=2)
+    klen = np.concatenate([length, length], axis=2)
+    q, v = _rand((1, 2, n, d), 90), _rand((1, 2, n, d), 91)
+    for bq, bk in ((16, 16), (32, 16), (16, 32)):
+        c = orc.bounds(q, k, frames, t, w, r, scale, bq, bk, center=True)
+        np.testing.assert_allclose(c["kmean"], mu0, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(c["kmax"], klen.reshape(1, 2, n // bk, bk).max(-1),
+                                   rtol=1e-10, atol=0)
+        for h in range(2):
+            for i in range(n):
+                vis = brute_visible(i // t, frames, w, r)
+                on = np.array([(j // t) in vis for j in range(n)])
+                qi = q[0, h, i]
+                bprime = scale * math.sqrt(sum(x * x for x in qi)) * klen[0, h, on].max()
+                shift = scale * sum(a * b for a, b in zip(qi, mu0[0, h])) + bprime
+                assert abs(c["row_bound"][0, h, i] - bprime) <= 1e-10 * bprime
+                assert abs(c["row_shift"][0, h, i] - shift) <= 1e-9 * (abs(shift) + 1.0)
+                s = scale * (k[0, h] @ qi)
+                assert np.all(s[on] <= c["row_shift"][0, h, i] + 1e-9)
+                assert np.all(s[on] >= c["row_shift"][0, h, i] - 2.0 * bprime - 1e-9)
+    # the offset makes the plain bound loose; centring makes it tight enough
+    plain = orc.bounds(q, k, frames, t, w, r, scale, 16, 16)
+    c = orc.bounds(q, k, frames, t, w, r, scale, 16, 16, center=True)
+    assert plain["eligible"].tolist() == [[0, 0]] and c["eligible"].tolist() == [[1, 1]]
+    assert np.all(plain["kmean"] == 0.0) and np.array_equal(plain["row_shift"], plain["row_bound"])
+    # the shifted softmax is the max-subtract softmax
+    a = orc.attention(q, k, v, frames, t, w, r, scale)
+    b = orc.attention_bound_shift(q, k, v, frames, t, w, r, scale, c["row_shift"])
+    np.testing.assert_allclose(b, a, rtol=0, atol=1e-12)
+    # translating every key by a vector moves the mean and the shift, not the bound
+    off = 10.0 * rng.standard_normal((1, 2, d))
+    c2 = orc.bounds(q, k + off[:, :, None, :], frames, t, w, r, scale, 16, 16, center=True)
+    np.testing.assert_allclose(c2["kmean"], c["kmean"] + off, rtol=0, atol=1e-11)
+    for key in ("kmax", "row_bound", "bmax"):
+        np.testing.assert_allclose(c2[key], c[key], rtol=1e-9, atol=0)
+    np.testing.assert_allclose(c2["row_shift"] - c["row_shift"],
+                               scale * np.einsum("bhnd,bhd->bhn", q, off), rtol=0, atol=1e-9)
+    # keys that already have mean zero: centring changes nothing
+    k0 = np.concatenate([dev, -dev], axis=2)
+    c0 = orc.bounds(q, k0, frames, t, w, r, scale, 16, 16, center=True)
+    p0 = orc.bounds(q, k0, frames, t, w, r, scale, 16, 16)
+    np.testing.assert_allclose(c0["kmean"], 0.0, rtol=0, atol=1e-15)
+    for key in ("kmax", "row_bound", "row_shift", "bmax"):
+        np.testing.assert_allclose(c0[key], p0[key], rtol=1e-12, atol=1e-13)
+
+
 ALL_CHECKS = [
     check_golden_attention, check_golden_plans, check_brute_force, check_weights,
     check_dense_limit, check_closed_forms, check_bound_shift_exact, check_cauchy_schwarz,
-    check_plan_closed_form, check_plan_negative_control, check_invariances,
+    check_plan_closed_form, check_plan_negative_control, check_invariances, check_centering,
 ]

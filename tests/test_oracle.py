@@ -85,6 +85,24 @@ def test_bound_stress_is_ineligible():
     assert np.isnan(b).any()
 
 
+@pytest.mark.slow
+def test_key_offset_centring_restores_eligibility():
+    """Keys sharing a 40-long offset push every plain bound above 32; centring
+    the keys brings it back under 32, and the centred shift equals
+    max-subtract within 1e-12 on sampled rows."""
+    wl = synthetic.WORKLOADS["key_offset"]
+    q, k, v = (synthetic.to_f64(t) for t in synthetic.make_inputs(wl))
+    args = (wl.frames, wl.tokens_per_frame, wl.window, wl.ref_frame, wl.scale)
+    plain = oracle.bounds(q, k, *args)
+    cent = oracle.bounds(q, k, *args, center=True)
+    assert np.all(plain["eligible"] == 0) and plain["bmax"].min() > 40.0
+    assert np.all(cent["eligible"] == 1) and cent["bmax"].max() < 25.0
+    rows = synthetic.sample_rows(wl, 24)
+    a = oracle.attention_rows(q, k, v, rows, *args)
+    b = oracle.attention_rows(q, k, v, rows, *args, row_bound=cent["row_shift"])
+    assert np.abs(a - b).max() < 1e-12
+
+
 def test_active_flops():
     assert oracle.active_flops(1, 2, 64, 5, 80, 1, 0) == 52_428_800
     assert oracle.active_flops(1, 8, 128, 21, 1200, 1, 0) == 471_859_200_000

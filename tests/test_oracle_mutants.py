@@ -57,8 +57,9 @@ def _attention_wrong_axis(q, k, v, frames, t, window, ref_frame, scale):
 
 
 def _bounds_kmin(q, k, frames, t, window, ref_frame, scale, block_q=0, block_k=0,
-                 bound_limit=32.0):
-    res = oracle.bounds(q, k, frames, t, window, ref_frame, scale, block_q, block_k, bound_limit)
+                 bound_limit=32.0, center=False):
+    res = oracle.bounds(q, k, frames, t, window, ref_frame, scale, block_q, block_k, bound_limit,
+                        center)
     info = res["info"]
     kn = np.sqrt((np.asarray(k, dtype=np.float64) ** 2).sum(-1))
     res["kmax"] = kn.reshape(*kn.shape[:2], info["n_kblocks"], info["block_k"]).min(-1)
@@ -66,8 +67,9 @@ def _bounds_kmin(q, k, frames, t, window, ref_frame, scale, block_q=0, block_k=0
 
 
 def _bounds_global(q, k, frames, t, window, ref_frame, scale, block_q=0, block_k=0,
-                   bound_limit=32.0):
-    res = oracle.bounds(q, k, frames, t, window, ref_frame, scale, block_q, block_k, bound_limit)
+                   bound_limit=32.0, center=False):
+    res = oracle.bounds(q, k, frames, t, window, ref_frame, scale, block_q, block_k, bound_limit,
+                        center)
     qn = res["qnorm"]
     kn = np.sqrt((np.asarray(k, dtype=np.float64) ** 2).sum(-1)).max(-1)
     res["row_bound"] = scale * qn * kn[..., None]
@@ -75,10 +77,50 @@ def _bounds_global(q, k, frames, t, window, ref_frame, scale, block_q=0, block_k
 
 
 def _bounds_no_sqrt(q, k, frames, t, window, ref_frame, scale, block_q=0, block_k=0,
-                    bound_limit=32.0):
-    res = oracle.bounds(q, k, frames, t, window, ref_frame, scale, block_q, block_k, bound_limit)
+                    bound_limit=32.0, center=False):
+    res = oracle.bounds(q, k, frames, t, window, ref_frame, scale, block_q, block_k, bound_limit,
+                        center)
     res["row_bound"] = res["row_bound"] * res["qnorm"]
     return res
+
+
+def _centred(fn):
+    """A bounds variant that applies ``fn(res, q, k, scale, mask_args)`` to centred results only."""
+    def bounds(q, k, frames, t, window, ref_frame, scale, block_q=0, block_k=0,
+               bound_limit=32.0, center=False):
+        res = oracle.bounds(q, k, frames, t, window, ref_frame, scale, block_q, block_k,
+                            bound_limit, center)
+        if center:
+            fn(res, np.asarray(q, dtype=np.float64), np.asarray(k, dtype=np.float64), scale,
+               (frames, t, window, ref_frame))
+        return res
+    return bounds
+
+
+def _shift_sign(res, q, k, scale, mask_args):
+    res["row_shift"] = res["row_bound"] - scale * np.einsum("bhnd,bhd->bhn", q, res["kmean"])
+
+
+def _shift_dropped(res, q, k, scale, mask_args):
+    res["row_shift"] = res["row_bound"].copy()
+
+
+def _uncentred_norms(res, q, k, scale, mask_args):
+    plain = oracle.bounds(q, k, *mask_args, scale, res["info"]["block_q"], res["info"]["block_k"])
+    res["kmax"] = plain["kmax"]
+    res["row_bound"] = plain["row_bound"]
+    res["row_shift"] = plain["row_bound"] + scale * np.einsum("bhnd,bhd->bhn", q, res["kmean"])
+
+
+def _block_mean(res, q, k, scale, mask_args):
+    bsz, heads, n, d = k.shape
+    bk = res["info"]["block_k"]
+    kb = k.reshape(bsz, heads, n // bk, bk, d)
+    res["kmax"] = np.sqrt(((kb - kb.mean(axis=3, keepdims=True)) ** 2).sum(-1)).max(-1)
+
+
+def _query_mean(res, q, k, scale, mask_args):
+    res["kmean"] = q.mean(axis=2)
 
 
 def _plan_descending(*args, **kw):
@@ -108,6 +150,11 @@ MUTANTS = {
     "key-block max taken as min": dict(ns={"bounds": _bounds_kmin}),
     "row bound over all keys": dict(ns={"bounds": _bounds_global}),
     "row bound with a squared query norm": dict(ns={"bounds": _bounds_no_sqrt}),
+    "centring shift with the wrong sign": dict(ns={"bounds": _centred(_shift_sign)}),
+    "centring shift dropped": dict(ns={"bounds": _centred(_shift_dropped)}),
+    "centred shift over uncentred key norms": dict(ns={"bounds": _centred(_uncentred_norms)}),
+    "key mean taken per key block": dict(ns={"bounds": _centred(_block_mean)}),
+    "query mean used as the key mean": dict(ns={"bounds": _centred(_query_mean)}),
     "key blocks listed descending": dict(ns={"plan": _plan_descending}),
     "query and key block sizes swapped": dict(ns={"plan": _plan_swapped_sizes}),
 }
