@@ -1,6 +1,6 @@
 """Benchmark of the frame-windowed sparse attention hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload sr720] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload sr720] [--no-cpu-baseline] [--center]
 
 One step is one pass of every stage of the path over one batch of synthetic
 input already resident in HBM: the host plan (fsa_plan into pinned memory and
@@ -19,6 +19,9 @@ between two device synchronisations. Prints ONE JSON line:
 * roofline.traffic: HBM bytes per launch from the committed rocprofv3
   FETCH_SIZE / WRITE_SIZE passes (profiles/traffic.json), reported only while
   the kernel source still matches the one those counters were taken on.
+
+--center runs fsa_bounds with key mean-centring (and fsa_attention with the
+resulting key mean); the default is off, as on the headline workload.
 
 Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -69,6 +72,8 @@ def parse():
                     help="heads of the workload the CPU oracle is timed on")
     ap.add_argument("--copies", type=int, default=3,
                     help="copies of q, k, v that consecutive steps rotate over")
+    ap.add_argument("--center", action="store_true",
+                    help="mean-centre the keys in fsa_bounds (key_offset workload)")
     return ap.parse_args()
 
 
@@ -141,6 +146,7 @@ def main():
     km = torch.empty((bsz, heads, info0.n_kblocks), dtype=torch.float32, device=dev)
     el = torch.empty((bsz, heads), dtype=torch.int32, device=dev)
     bm = torch.empty((bsz, heads), dtype=torch.float32, device=dev)
+    mu = torch.empty((bsz, heads, d), dtype=torch.float32, device=dev) if args.center else None
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
@@ -161,10 +167,10 @@ def main():
         copied[slot] = e
         if ev is not None:
             ev[0].record(stream)
-        fsa.bounds(dplan, q, k, wl.scale, 0.0, 0, 0, qn, km, el, bm, stream=stream)
+        fsa.bounds(dplan, q, k, wl.scale, 0.0, 0, 0, qn, km, el, bm, stream=stream, kmean=mu)
         if ev is not None:
             ev[1].record(stream)
-        fsa.attention(dplan, q, k, v, qn, km, el, wl.scale, 0, 0, out=o, stream=stream)
+        fsa.attention(dplan, q, k, v, qn, km, el, wl.scale, 0, 0, out=o, stream=stream, kmean=mu)
         if ev is not None:
             ev[2].record(stream)
 
@@ -191,7 +197,11 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     attn_mean = float(attn_ms.mean())
     achieved = flops / (attn_mean * 1e-3) / 1e12
+    # q and k read once, the norm arrays written; centring reads k once more
+    # (the mean must be known before the centred norms) and writes the mean
     bounds_bytes = 2 * bsz * heads * n * d * 2 + 4 * bsz * heads * (n + info0.n_kblocks + 2)
+    if args.center:
+        bounds_bytes += bsz * heads * n * d * 2 + 4 * bsz * heads * d
     eligible = el.cpu().numpy()
 
     line = {
@@ -212,7 +222,7 @@ def main():
             "frames": wl.frames, "tokens_per_frame": wl.tokens_per_frame, "seq_len": wl.seq_len,
             "window": wl.window, "ref_frame": wl.ref_frame, "block_q": info0.block_q,
             "block_k": info0.block_k, "nnz": info0.nnz, "active_flops": flops,
-            "eligible_heads": int(eligible.sum()),
+            "eligible_heads": int(eligible.sum()), "key_centring": bool(args.center),
         },
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {

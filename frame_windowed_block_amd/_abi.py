@@ -71,10 +71,10 @@ def lib() -> ctypes.CDLL:
                                _I32P, _I64, _I32P, _I64]
         L.fsa_bounds.restype = ctypes.c_int
         L.fsa_bounds.argtypes = [ctypes.POINTER(PlanInfo), _P, _P, _P, _P, _I32, _I32, _I32,
-                                 _I32, _I32, _F32, _F32, _P, _P, _P, _P, _P]
+                                 _I32, _I32, _F32, _F32, _P, _P, _P, _P, _P, _P]
         L.fsa_attention.restype = ctypes.c_int
         L.fsa_attention.argtypes = [ctypes.POINTER(PlanInfo), _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                    _I32, _I32, _I32, _F32, _I32, _I32, _P]
+                                    _P, _I32, _I32, _I32, _F32, _I32, _I32, _P]
         _lib = L
     return _lib
 
@@ -152,9 +152,11 @@ class DevicePlan:
 
 def bounds(dplan: DevicePlan, q, k, scale: float, bound_limit: float = 0.0,
            head_offset: int = 0, head_count: int = 0,
-           qnorm=None, kmax=None, eligible=None, bmax=None, stream=None):
+           qnorm=None, kmax=None, eligible=None, bmax=None, stream=None,
+           kmean=None, center: bool = False):
     """fsa_bounds. Returns (qnorm fp32 [B,H,N], kmax fp32 [B,H,n_kb],
-    eligible int32 [B,H], bmax fp32 [B,H])."""
+    eligible int32 [B,H], bmax fp32 [B,H], kmean fp32 [B,H,D] or None).
+    Keys are mean-centred when ``center`` is set or a ``kmean`` buffer is given."""
     torch = _torch()
     _check_qkv("q", q)
     _check_qkv("k", k, q.shape)
@@ -169,16 +171,19 @@ def bounds(dplan: DevicePlan, q, k, scale: float, bound_limit: float = 0.0,
         eligible = torch.empty((bsz, heads), dtype=torch.int32, device=dev)
     if bmax is None:
         bmax = torch.empty((bsz, heads), dtype=torch.float32, device=dev)
+    if center and kmean is None:
+        kmean = torch.empty((bsz, heads, d), dtype=torch.float32, device=dev)
     _check(lib().fsa_bounds(ctypes.byref(info), _ptr(dplan.row_ptr), _ptr(dplan.col_idx),
                             _ptr(q), _ptr(k), bsz, heads, d, head_offset, head_count,
                             float(scale), float(bound_limit), _ptr(qnorm), _ptr(kmax),
-                            _ptr(eligible), _ptr(bmax), _stream_handle(stream)))
-    return qnorm, kmax, eligible, bmax
+                            _ptr(eligible), _ptr(bmax), _ptr(kmean), _stream_handle(stream)))
+    return qnorm, kmax, eligible, bmax, kmean
 
 
 def attention(dplan: DevicePlan, q, k, v, qnorm, kmax, eligible, scale: float,
-              head_offset: int = 0, head_count: int = 0, out=None, stream=None):
-    """fsa_attention. Returns o (bf16 [B,H,N,D])."""
+              head_offset: int = 0, head_count: int = 0, out=None, stream=None, kmean=None):
+    """fsa_attention. Returns o (bf16 [B,H,N,D]). ``kmean`` is the key mean of a
+    centred fsa_bounds call, or None."""
     torch = _torch()
     _check_qkv("q", q)
     _check_qkv("k", k, q.shape)
@@ -191,15 +196,17 @@ def attention(dplan: DevicePlan, q, k, v, qnorm, kmax, eligible, scale: float,
     info = dplan.info
     _check(lib().fsa_attention(ctypes.byref(info), _ptr(dplan.row_ptr), _ptr(dplan.col_idx),
                                _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(qnorm), _ptr(kmax),
-                               _ptr(eligible), bsz, heads, d, float(scale), head_offset,
+                               _ptr(eligible), _ptr(kmean), bsz, heads, d, float(scale), head_offset,
                                head_count, _stream_handle(stream)))
     return out
 
 
 def forward(dplan: DevicePlan, q, k, v, scale: float, bound_limit: float = 0.0,
-            head_offset: int = 0, head_count: int = 0, out=None, stream=None):
+            head_offset: int = 0, head_count: int = 0, out=None, stream=None,
+            center: bool = False):
     """fsa_bounds then fsa_attention on the same stream. Returns (o, bounds tuple)."""
-    b = bounds(dplan, q, k, scale, bound_limit, head_offset, head_count, stream=stream)
+    b = bounds(dplan, q, k, scale, bound_limit, head_offset, head_count, stream=stream,
+               center=center)
     o = attention(dplan, q, k, v, b[0], b[1], b[2], scale, head_offset, head_count,
-                  out=out, stream=stream)
+                  out=out, stream=stream, kmean=b[4])
     return o, b

@@ -51,7 +51,8 @@ fsa_status check_csr(const int32_t *row_ptr, const int32_t *col_idx) {
     return FSA_OK;
 }
 
-fsa_status check_bf16(const void *p, const char *name) {
+// bf16 tensors and the fp32 key mean are read 16 bytes at a time
+fsa_status check_vec16(const void *p, const char *name) {
     if (!p) return fail(FSA_ERR_INVALID_ARG, "%s is NULL", name);
     if (!aligned(p, 16)) return fail(FSA_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
     return FSA_OK;
@@ -77,7 +78,8 @@ extern "C" {
 fsa_status fsa_bounds(const fsa_plan_info *plan, const int32_t *d_row_ptr, const int32_t *d_col_idx,
                       const void *q, const void *k, int32_t batch, int32_t heads, int32_t head_dim,
                       int32_t head_offset, int32_t head_count, float scale, float bound_limit,
-                      float *qnorm, float *kmax, int32_t *eligible, float *bmax, void *stream) {
+                      float *qnorm, float *kmax, int32_t *eligible, float *bmax, float *kmean,
+                      void *stream) {
     using namespace fsa;
     clear_error();
     int32_t hc = 0;
@@ -85,18 +87,19 @@ fsa_status fsa_bounds(const fsa_plan_info *plan, const int32_t *d_row_ptr, const
     FSA_TRY(check_common(plan, batch, heads, head_dim, head_offset, head_count, scale, &hc, &empty));
     if (empty) return FSA_OK;
     FSA_TRY(check_csr(d_row_ptr, d_col_idx));
-    FSA_TRY(check_bf16(q, "q"));
-    FSA_TRY(check_bf16(k, "k"));
+    FSA_TRY(check_vec16(q, "q"));
+    FSA_TRY(check_vec16(k, "k"));
     FSA_TRY(check_word(qnorm, "qnorm"));
     FSA_TRY(check_word(kmax, "kmax"));
     FSA_TRY(check_word(eligible, "eligible"));
     FSA_TRY(check_word(bmax, "bmax"));
+    if (kmean) FSA_TRY(check_vec16(kmean, "kmean"));
     const int64_t units = int64_t(batch) * hc * (plan->seq_len / 16 + plan->n_kblocks);
     if (units / 4 + 1 > kMaxWorkgroups || int64_t(batch) * hc * plan->n_qblocks > kMaxWorkgroups)
         return fail(FSA_ERR_UNSUPPORTED, "problem needs more workgroups than one launch holds");
     if (!(bound_limit > 0.0f)) bound_limit = 32.0f;               // <= 0 or NaN: default
     BoundsLaunch a{plan, d_row_ptr, d_col_idx, q, k, batch, heads, head_dim, head_offset, hc,
-                   scale, bound_limit, qnorm, kmax, eligible, bmax, stream};
+                   scale, bound_limit, qnorm, kmax, eligible, bmax, kmean, stream};
     const int err = launch_bounds(a);
     if (err) return fail(FSA_ERR_HIP, "fsa_bounds launch failed: %s", hip_error_text(err));
     return FSA_OK;
@@ -105,7 +108,7 @@ fsa_status fsa_bounds(const fsa_plan_info *plan, const int32_t *d_row_ptr, const
 fsa_status fsa_attention(const fsa_plan_info *plan, const int32_t *d_row_ptr, const int32_t *d_col_idx,
                          const void *q, const void *k, const void *v, void *o,
                          const float *qnorm, const float *kmax, const int32_t *eligible,
-                         int32_t batch, int32_t heads, int32_t head_dim, float scale,
+                         const float *kmean, int32_t batch, int32_t heads, int32_t head_dim, float scale,
                          int32_t head_offset, int32_t head_count, void *stream) {
     using namespace fsa;
     clear_error();
@@ -114,13 +117,14 @@ fsa_status fsa_attention(const fsa_plan_info *plan, const int32_t *d_row_ptr, co
     FSA_TRY(check_common(plan, batch, heads, head_dim, head_offset, head_count, scale, &hc, &empty));
     if (empty) return FSA_OK;
     FSA_TRY(check_csr(d_row_ptr, d_col_idx));
-    FSA_TRY(check_bf16(q, "q"));
-    FSA_TRY(check_bf16(k, "k"));
-    FSA_TRY(check_bf16(v, "v"));
-    FSA_TRY(check_bf16(o, "o"));
+    FSA_TRY(check_vec16(q, "q"));
+    FSA_TRY(check_vec16(k, "k"));
+    FSA_TRY(check_vec16(v, "v"));
+    FSA_TRY(check_vec16(o, "o"));
     FSA_TRY(check_word(qnorm, "qnorm"));
     FSA_TRY(check_word(kmax, "kmax"));
     FSA_TRY(check_word(eligible, "eligible"));
+    if (kmean) FSA_TRY(check_vec16(kmean, "kmean"));
     // o must not overlap an input: the kernel reads q, k, v while writing o
     const int64_t bytes = int64_t(batch) * heads * plan->seq_len * head_dim * 2;
     const uintptr_t ob = reinterpret_cast<uintptr_t>(o);
@@ -131,7 +135,7 @@ fsa_status fsa_attention(const fsa_plan_info *plan, const int32_t *d_row_ptr, co
     }
     if (int64_t(batch) * hc * plan->n_qblocks + 8 > kMaxWorkgroups)
         return fail(FSA_ERR_UNSUPPORTED, "problem needs more workgroups than one launch holds");
-    AttentionLaunch a{plan, d_row_ptr, d_col_idx, q, k, v, o, qnorm, kmax, eligible,
+    AttentionLaunch a{plan, d_row_ptr, d_col_idx, q, k, v, o, qnorm, kmax, eligible, kmean,
                       batch, heads, head_dim, head_offset, hc, scale, stream};
     const int err = launch_attention(a);
     if (err) return fail(FSA_ERR_HIP, "fsa_attention launch failed: %s", hip_error_text(err));

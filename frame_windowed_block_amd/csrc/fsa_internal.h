@@ -29,6 +29,7 @@ struct BoundsLaunch {
     float *qnorm, *kmax;
     int32_t *eligible;
     float *bmax;
+    float *kmean;            // NULL: no key centring
     void *stream;
 };
 
@@ -39,6 +40,7 @@ struct AttentionLaunch {
     void *o;
     const float *qnorm, *kmax;
     const int32_t *eligible;
+    const float *kmean;      // NULL: no key centring
     int32_t batch, heads, head_dim, head_offset, head_count;
     float scale;
     void *stream;

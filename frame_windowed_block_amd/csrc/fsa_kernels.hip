@@ -7,9 +7,11 @@
 //   [uk:Softmax] bib.com.ua, "HeyGen прискорила Avatar IV на TPU у 1,86 раза",
 //                section on breaking the softmax serial chain.
 //
-// fsa_bounds runs two kernels. norms_kernel streams q and k once (the HBM-bound
-// part): it writes ||q_i|| per row and, per key block, the largest ||k_j||
-// ("a small array of precomputed norms", [vi:Softmax]). bound_reduce_kernel
+// fsa_bounds runs two kernels (four with key centring, which first reduces the
+// keys of each head to their mean in two fixed-order kernels). norms_kernel
+// streams q and k once (the HBM-bound part): it writes ||q_i|| per row and,
+// per key block, the largest ||k_j|| (of k_j - mean when centred) ("a small
+// array of precomputed norms", [vi:Softmax]). bound_reduce_kernel
 // then derives, per query block, scale * max ||q_i|| * max kmax over the
 // block's active key blocks, folds it into the head's largest row bound, and
 // the last block of each head writes the head's eligibility ([vi:Softmax]:
@@ -28,7 +30,7 @@
 //   P   = exp2(S * scale * log2e - B_i * log2e)
 //                     B_i = scale * ||q_i|| * max kmax over the row's active
 //                     key blocks, fixed before the loop ([vi:Softmax]); no
-//                     running max, no rescale
+//                     running max, no rescale (centred keys add scale q_i.mean)
 //   O^T += V^T P^T    bf16 MFMA 32x32x16, V^T read from row-major V in LDS
 //                     with the transposing LDS reads
 // The scores of sub-step j + 1 are computed in the same step as the weights
@@ -72,11 +74,107 @@ __device__ __forceinline__ float sumsq8(u32x4 x) {
     return s;
 }
 
+// Sum of squares of (x - m) over 8 bf16 values and their 8 fp32 offsets.
+__device__ __forceinline__ float sumsq8_centred(u32x4 x, const float (&m)[8]) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float a = bf16_lo(x[i]) - m[2 * i], b = bf16_hi(x[i]) - m[2 * i + 1];
+        s = fmaf(a, a, s);
+        s = fmaf(b, b, s);
+    }
+    return s;
+}
+
 // Max that lets a NaN through (a NaN norm must make the head ineligible).
 __device__ __forceinline__ float nan_max(float a, float b) { return (b > a || b != b) ? b : a; }
 
 // --------------------------------------------------------------------------
-// fsa_bounds, kernel 1: row norms of q, largest key norm per key block.
+// fsa_bounds with key centring ([vi:Softmax]: the keys share a large common
+// component; removing the mean key tightens the bound), kernels 0a and 0b:
+// the mean of each head's N keys, summed in a fixed order so that the result
+// is deterministic. 0a sums chunks of 2D consecutive keys into D fp32
+// partials; with more than one chunk per head the partials are parked in the
+// head's own qnorm rows (chunks * D <= N, and the norms kernel overwrites them
+// later in stream order) and 0b adds them up.
+// --------------------------------------------------------------------------
+struct KeySumParams {
+    const uint16_t *k;
+    float *partial;      // qnorm of the head range, used as scratch
+    float *kmean;
+    int32_t heads, seq_len, h0, hc, chunks;
+};
+
+template <int D>
+constexpr int key_chunk() { return 2 * D; }
+
+template <int D>
+__global__ __launch_bounds__(256) void key_sum_kernel(KeySumParams p) {
+    constexpr int LPR = D / 8;              // lanes per key row, 16 bytes each
+    constexpr int RPP = 256 / LPR;          // key rows per pass of the workgroup
+    constexpr int PASSES = key_chunk<D>() / RPP;
+    __shared__ float part[RPP * D];
+    const int tid = threadIdx.x, sub = tid / LPR, seg = tid % LPR;
+    const int64_t bh = blockIdx.x / p.chunks;
+    const int32_t chunk = int32_t(blockIdx.x % p.chunks);
+    const int64_t hb = (bh / p.hc) * p.heads + p.h0 + bh % p.hc;
+    const int32_t r0 = chunk * key_chunk<D>();
+    const int32_t rows = min(key_chunk<D>(), p.seq_len - r0);
+    const uint16_t *base = p.k + (hb * p.seq_len + r0) * D + seg * 8;
+    u32x4 x[PASSES];
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+        const int r = ps * RPP + sub;
+        x[ps] = *reinterpret_cast<const u32x4 *>(base + int64_t(r < rows ? r : rows - 1) * D);
+    }
+    float acc[8] = {};
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+        if (ps * RPP + sub < rows) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] += bf16_lo(x[ps][i]);
+                acc[2 * i + 1] += bf16_hi(x[ps][i]);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[sub * D + seg * 8 + i] = acc[i];
+    __syncthreads();
+    if (tid < D) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < RPP; ++r) sum += part[r * D + tid];
+        if (p.chunks == 1)
+            p.kmean[hb * D + tid] = sum / float(p.seq_len);
+        else
+            p.partial[hb * p.seq_len + int64_t(chunk) * D + tid] = sum;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(1024) void key_mean_kernel(KeySumParams p) {
+    constexpr int S = 1024 / D;             // interleaved subsets of the chunks
+    __shared__ float part[1024];
+    const int tid = threadIdx.x, d = tid % D, sub = tid / D;
+    const int64_t bh = blockIdx.x;
+    const int64_t hb = (bh / p.hc) * p.heads + p.h0 + bh % p.hc;
+    const float *src = p.partial + hb * p.seq_len + d;
+    float sum = 0.0f;
+    for (int32_t c = sub; c < p.chunks; c += S) sum += src[int64_t(c) * D];
+    part[tid] = sum;
+    __syncthreads();
+    if (tid < D) {
+        float total = 0.0f;
+#pragma unroll
+        for (int j = 0; j < S; ++j) total += part[j * D + tid];
+        p.kmean[hb * D + tid] = total / float(p.seq_len);
+    }
+}
+
+// --------------------------------------------------------------------------
+// fsa_bounds, kernel 1: row norms of q, largest key norm per key block (of
+// the centred keys k_j - mean when CENTRED).
 // Work unit = one wavefront: either QG 16-row groups of q, or one key block.
 // --------------------------------------------------------------------------
 struct NormsParams {
@@ -84,11 +182,12 @@ struct NormsParams {
     float *qnorm, *kmax;
     int32_t *eligible;
     float *bmax;
+    const float *kmean;
     int64_t q_units, total_units;
     int32_t batch, heads, seq_len, h0, hc, block_k, n_kb;
 };
 
-template <int D, int QG>
+template <int D, int QG, bool CENTRED>
 __global__ __launch_bounds__(256) void norms_kernel(NormsParams p) {
     constexpr int LPR = D / 8;          // lanes per row: 16 bytes each
     constexpr int RPL = 64 / LPR;       // rows covered by one wave-wide load
@@ -147,6 +246,14 @@ __global__ __launch_bounds__(256) void norms_kernel(NormsParams p) {
         const int64_t hb = (bh / p.hc) * p.heads + p.h0 + bh % p.hc;
         const uint16_t *base = p.k + (hb * p.seq_len + kb * p.block_k) * D;
         const int groups = p.block_k / 16;
+        float mu[8] = {};
+        if constexpr (CENTRED) {
+            const float4 m0 = *reinterpret_cast<const float4 *>(p.kmean + hb * D + seg * 8);
+            const float4 m1 = *reinterpret_cast<const float4 *>(p.kmean + hb * D + seg * 8 + 4);
+            mu[0] = m0.x; mu[1] = m0.y; mu[2] = m0.z; mu[3] = m0.w;
+            mu[4] = m1.x; mu[5] = m1.y; mu[6] = m1.z; mu[7] = m1.w;
+        }
+        auto ksq = [&](u32x4 v) { return CENTRED ? sumsq8_centred(v, mu) : sumsq8(v); };
         float best = 0.0f;     // largest squared row norm seen by this lane's rows
         int gi = 0;
         for (; gi + 2 <= groups; gi += 2) {
@@ -161,7 +268,7 @@ __global__ __launch_bounds__(256) void norms_kernel(NormsParams p) {
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int l = 0; l < LOADS; ++l) {
-                    float s = sumsq8(x[j][l]);
+                    float s = ksq(x[j][l]);
 #pragma unroll
                     for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
                     best = nan_max(best, s);
@@ -174,7 +281,7 @@ __global__ __launch_bounds__(256) void norms_kernel(NormsParams p) {
                 x[l] = *reinterpret_cast<const u32x4 *>(base + int64_t(gi * 16 + l * RPL + sub) * D + seg * 8);
 #pragma unroll
             for (int l = 0; l < LOADS; ++l) {
-                float s = sumsq8(x[l]);
+                float s = ksq(x[l]);
 #pragma unroll
                 for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
                 best = nan_max(best, s);
@@ -252,6 +359,7 @@ struct AttnParams {
     uint16_t *o;
     const float *qnorm, *kmax;
     const int32_t *eligible, *row_ptr, *col_idx;
+    const float *kmean;     // key mean per head when the bounds were centred, else null
     int64_t total_wg, per_xcd;
     int32_t heads, seq_len, h0, hc;
     int32_t frames, tokens_per_frame, block_q, block_k, n_qb, n_kb;
@@ -647,7 +755,8 @@ struct AttnKernel {
     template <int NG>
     static __device__ __forceinline__ void tile(const AttnParams &p, char *smem, int64_t head_row0, int32_t row0,
                                                 int nvalid, const uint16_t *kh, const uint16_t *vh, int32_t e0,
-                                                int32_t e1, int32_t nquart, bool online, float mk) {
+                                                int32_t e1, int32_t nquart, bool online, float mk,
+                                                const float *mu) {
         const int lane = threadIdx.x & 63;
         const int n = lane & 31, h = lane >> 5;
         const int32_t row = row0 + (n < nvalid ? n : nvalid - 1);   // rows past the tile recompute a valid one
@@ -661,7 +770,33 @@ struct AttnKernel {
             for (int ks = 0; ks < G::KS; ++ks) rw.qf[ks] = *reinterpret_cast<const bf16x8 *>(qr + 16 * ks + 8 * h);
 #pragma unroll
             for (int dt = 0; dt < G::DT; ++dt) rw.acc[dt] = f32x16{};
-            if (!online) rw.brow = p.c * p.qnorm[head_row0 + row] * mk;
+            if (!online) {
+                float shift = p.qnorm[head_row0 + row] * mk;
+                if (mu) {
+                    // centred keys: s_ij = scale q_i.mu + scale q_i.(k_j - mu), and the
+                    // bound covers the second term; add this row's q_i.mu. Each half of
+                    // the wavefront holds half of the row's columns.
+                    float part = 0.0f;
+#pragma unroll
+                    for (int ks = 0; ks < G::KS; ++ks) {
+                        const float4 m0 = *reinterpret_cast<const float4 *>(mu + 16 * ks + 8 * h);
+                        const float4 m1 = *reinterpret_cast<const float4 *>(mu + 16 * ks + 8 * h + 4);
+                        const bf16x8 x = rw.qf[ks];
+                        part = fmaf(float(x[0]), m0.x, part);
+                        part = fmaf(float(x[1]), m0.y, part);
+                        part = fmaf(float(x[2]), m0.z, part);
+                        part = fmaf(float(x[3]), m0.w, part);
+                        part = fmaf(float(x[4]), m1.x, part);
+                        part = fmaf(float(x[5]), m1.y, part);
+                        part = fmaf(float(x[6]), m1.z, part);
+                        part = fmaf(float(x[7]), m1.w, part);
+                    }
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
+                                                                     __float_as_uint(part), false, false);
+                    shift += __uint_as_float(sw[0]) + __uint_as_float(sw[1]);   // same value in both halves
+                }
+                rw.brow = p.c * shift;
+            }
         }
         if (online)
             walk<NG, true>(p, smem, kh, vh, e0, e1, nquart, rw);
@@ -713,6 +848,7 @@ struct AttnKernel {
         const int32_t e1 = __builtin_amdgcn_readfirstlane(p.row_ptr[qb + 1]);
         const int32_t nquart = (e1 - e0) * (p.block_k / 16);
         const bool online = __builtin_amdgcn_readfirstlane(p.eligible[hb]) == 0;
+        const float *mu = p.kmean ? p.kmean + hb * D : nullptr;
 
         // bound path: largest key norm over the row's active key blocks
         float mk = 0.0f;
@@ -734,9 +870,9 @@ struct AttnKernel {
             const int32_t row0 = qb * p.block_q + 32 * my;
             const int nvalid = p.block_q - 32 * my < 32 ? p.block_q - 32 * my : 32;
             if (my < ntiles)
-                tile<1>(p, smem, head_row0, row0, nvalid, kh, vh, e0, e1, nquart, online, mk);
+                tile<1>(p, smem, head_row0, row0, nvalid, kh, vh, e0, e1, nquart, online, mk, mu);
             else
-                tile<0>(p, smem, head_row0, row0, nvalid, kh, vh, e0, e1, nquart, online, mk);
+                tile<0>(p, smem, head_row0, row0, nvalid, kh, vh, e0, e1, nquart, online, mk, mu);
             if (t0 + NW < ntiles) lds_barrier();     // LDS reused by the next pass
         }
     }
@@ -756,6 +892,35 @@ int launch_bounds(const BoundsLaunch &a) {
     const fsa_plan_info &pl = *a.plan;
     hipStream_t stream = static_cast<hipStream_t>(a.stream);
     constexpr int QG = 2;
+    const int64_t nbh = int64_t(a.batch) * a.head_count;
+    hipError_t err = hipSuccess;
+    if (a.kmean) {
+        KeySumParams kp;
+        kp.k = static_cast<const uint16_t *>(a.k);
+        kp.partial = a.qnorm;
+        kp.kmean = a.kmean;
+        kp.heads = a.heads;
+        kp.seq_len = pl.seq_len;
+        kp.h0 = a.head_offset;
+        kp.hc = a.head_count;
+        const int chunk = a.head_dim == 128 ? key_chunk<128>() : key_chunk<64>();
+        kp.chunks = (pl.seq_len + chunk - 1) / chunk;      // > 1 only when N > 2D, so chunks * D <= N
+        const unsigned grid0 = unsigned(nbh * kp.chunks);
+        if (a.head_dim == 128)
+            hipLaunchKernelGGL(key_sum_kernel<128>, dim3(grid0), dim3(256), 0, stream, kp);
+        else
+            hipLaunchKernelGGL(key_sum_kernel<64>, dim3(grid0), dim3(256), 0, stream, kp);
+        err = hipGetLastError();
+        if (err != hipSuccess) return int(err);
+        if (kp.chunks > 1) {
+            if (a.head_dim == 128)
+                hipLaunchKernelGGL(key_mean_kernel<128>, dim3(unsigned(nbh)), dim3(1024), 0, stream, kp);
+            else
+                hipLaunchKernelGGL(key_mean_kernel<64>, dim3(unsigned(nbh)), dim3(1024), 0, stream, kp);
+            err = hipGetLastError();
+            if (err != hipSuccess) return int(err);
+        }
+    }
     NormsParams np;
     np.q = static_cast<const uint16_t *>(a.q);
     np.k = static_cast<const uint16_t *>(a.k);
@@ -763,7 +928,7 @@ int launch_bounds(const BoundsLaunch &a) {
     np.kmax = a.kmax;
     np.eligible = a.eligible;
     np.bmax = a.bmax;
-    const int64_t nbh = int64_t(a.batch) * a.head_count;
+    np.kmean = a.kmean;
     np.q_units = nbh * ((pl.seq_len / 16 + QG - 1) / QG);
     np.total_units = np.q_units + nbh * pl.n_kblocks;
     np.batch = a.batch;
@@ -774,11 +939,18 @@ int launch_bounds(const BoundsLaunch &a) {
     np.block_k = pl.block_k;
     np.n_kb = pl.n_kblocks;
     const unsigned grid1 = unsigned((np.total_units + 3) / 4);
-    if (a.head_dim == 128)
-        hipLaunchKernelGGL((norms_kernel<128, QG>), dim3(grid1), dim3(256), 0, stream, np);
-    else
-        hipLaunchKernelGGL((norms_kernel<64, QG>), dim3(grid1), dim3(256), 0, stream, np);
-    hipError_t err = hipGetLastError();
+    if (a.head_dim == 128) {
+        if (a.kmean)
+            hipLaunchKernelGGL((norms_kernel<128, QG, true>), dim3(grid1), dim3(256), 0, stream, np);
+        else
+            hipLaunchKernelGGL((norms_kernel<128, QG, false>), dim3(grid1), dim3(256), 0, stream, np);
+    } else {
+        if (a.kmean)
+            hipLaunchKernelGGL((norms_kernel<64, QG, true>), dim3(grid1), dim3(256), 0, stream, np);
+        else
+            hipLaunchKernelGGL((norms_kernel<64, QG, false>), dim3(grid1), dim3(256), 0, stream, np);
+    }
+    err = hipGetLastError();
     if (err != hipSuccess) return int(err);
 
     ReduceParams rp;
@@ -839,6 +1011,7 @@ int launch_attention(const AttentionLaunch &a) {
     p.qnorm = a.qnorm;
     p.kmax = a.kmax;
     p.eligible = a.eligible;
+    p.kmean = a.kmean;
     p.row_ptr = a.row_ptr;
     p.col_idx = a.col_idx;
     p.total_wg = int64_t(a.batch) * a.head_count * pl.n_qblocks;

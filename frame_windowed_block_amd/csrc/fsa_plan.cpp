@@ -125,7 +125,7 @@ fsa_status check_plan_info(const fsa_plan_info *p) {
 
 extern "C" {
 
-int32_t fsa_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+int32_t fsa_version(void) { return 1 * 10000 + 1 * 100 + 0; }
 
 const char *fsa_status_string(fsa_status status) {
     switch (status) {

@@ -15,7 +15,9 @@
  *   fsa_bounds     the small precomputed norm array behind the softmax bound
  *                  (section "Giải phóng Softmax"): per-row query norms,
  *                  per-key-block largest key norms, and the per-head check of
- *                  whether the bound is tight enough to use.
+ *                  whether the bound is tight enough to use; optionally with
+ *                  the keys mean-centred first (same section), which tightens
+ *                  the bound when the keys share a large common component.
  *   fsa_attention  one pass of q, k, v -> o over the whole mask (window and
  *                  reference frame together, no second pass, no merge),
  *                  with each row's softmax shifted by its Cauchy-Schwarz bound
@@ -123,14 +125,24 @@ fsa_status fsa_plan(int32_t frames, int32_t tokens_per_frame, int32_t window, in
  *   bmax     fp32 [B, H]        largest row bound B_i = scale * ||q_i|| *
  *                               (largest kmax over the key blocks active for
  *                               the query block holding i)
- * eligible and bmax also serve as the call's own accumulators while it runs:
- * their values are defined only once the stream has completed the call.
+ *   kmean    NULL, or fp32 [B, H, D], 16-byte aligned: key mean-centring (section "Giải phóng
+ *            Softmax": the keys share a large common component; removing the
+ *            mean key tightens the bound and leaves the softmax unchanged).
+ *            When given, the call writes the mean of the head's N keys,
+ *            mu = (1/N) sum_j k_j, and kmax becomes the largest ||k_j - mu||
+ *            over key block kb, so B_i, bmax and eligible use the centred
+ *            norms. NULL: no centring (kmax as above).
+ * eligible and bmax also serve as the call's own accumulators while it runs,
+ * and with kmean the head range of qnorm holds partial key sums until the call
+ * overwrites it with the norms: their values are defined only once the stream
+ * has completed the call.
  * B == 0 or an empty head range is a no-op returning FSA_OK.
  */
 fsa_status fsa_bounds(const fsa_plan_info *plan, const int32_t *d_row_ptr, const int32_t *d_col_idx,
                       const void *q, const void *k, int32_t batch, int32_t heads, int32_t head_dim,
                       int32_t head_offset, int32_t head_count, float scale, float bound_limit,
-                      float *qnorm, float *kmax, int32_t *eligible, float *bmax, void *stream);
+                      float *qnorm, float *kmax, int32_t *eligible, float *bmax, float *kmean,
+                      void *stream);
 
 /*
  * fsa_attention - one pass of frame-windowed sparse attention (sections
@@ -141,15 +153,19 @@ fsa_status fsa_bounds(const fsa_plan_info *plan, const int32_t *d_row_ptr, const
  * of i's query block, with p_ij = exp(s_ij - B_i), s_ij = scale * q_i . k_j
  * and B_i = scale * qnorm_i * max kmax over those blocks, for heads with
  * eligible = 1; heads with eligible = 0 use the running row max instead.
- * Both are masked softmax attention in exact arithmetic. Accumulation is fp32;
+ * With key centring the bound-path shift is B_i + scale * q_i . mu instead
+ * (the centred scores scale * q_i . (k_j - mu) shifted by their bound B_i).
+ * All are masked softmax attention in exact arithmetic. Accumulation is fp32;
  * p is rounded to bf16 for the p.v product; o is rounded to bf16 (RNE).
  *
  * plan, d_row_ptr, d_col_idx: as for fsa_bounds (the CSR must be the one
  *             fsa_plan produced for `plan`).
  * q, k, v:    device bf16 [B, H, N, D] inputs; o: device bf16 [B, H, N, D]
  *             output; all 16-byte aligned; o must not overlap the inputs.
- * qnorm, kmax, eligible: the outputs of fsa_bounds for the same q, k, scale
- *             and head range (only the range is read).
+ * qnorm, kmax, eligible, kmean: the outputs of fsa_bounds for the same q, k,
+ *             scale and head range (only the range is read). kmean must be
+ *             NULL exactly when that fsa_bounds call had NULL: centred norms
+ *             with an uncentred shift (or the reverse) are not a bound.
  * head_dim:   64 or 128 (else FSA_ERR_UNSUPPORTED).
  * head_offset, head_count: as for fsa_bounds; rows of other heads in o are
  *             not written, so several calls on disjoint head ranges may run
@@ -160,7 +176,7 @@ fsa_status fsa_bounds(const fsa_plan_info *plan, const int32_t *d_row_ptr, const
 fsa_status fsa_attention(const fsa_plan_info *plan, const int32_t *d_row_ptr, const int32_t *d_col_idx,
                          const void *q, const void *k, const void *v, void *o,
                          const float *qnorm, const float *kmax, const int32_t *eligible,
-                         int32_t batch, int32_t heads, int32_t head_dim, float scale,
+                         const float *kmean, int32_t batch, int32_t heads, int32_t head_dim, float scale,
                          int32_t head_offset, int32_t head_count, void *stream);
 
 /* Static English text for a status code (never NULL). */

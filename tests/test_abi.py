@@ -18,7 +18,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert fsa.version() == 10000
+    assert fsa.version() == 10100
     L = fsa.lib()
     for code in range(6):
         assert L.fsa_status_string(code)
@@ -36,26 +36,27 @@ FAKE = 0x10000          # a 64 KiB-aligned address that is never dereferenced
 def _bounds(info, **kw):
     args = dict(row_ptr=FAKE, col_idx=FAKE, q=FAKE, k=FAKE, batch=1, heads=2, head_dim=64,
                 head_offset=0, head_count=0, scale=0.125, bound_limit=0.0, qnorm=FAKE,
-                kmax=FAKE, eligible=FAKE, bmax=FAKE)
+                kmax=FAKE, eligible=FAKE, bmax=FAKE, kmean=0)
     args.update(kw)
     L = fsa.lib()
     st = L.fsa_bounds(ctypes.byref(info) if info is not None else None,
                       args["row_ptr"], args["col_idx"], args["q"], args["k"], args["batch"],
                       args["heads"], args["head_dim"], args["head_offset"], args["head_count"],
                       args["scale"], args["bound_limit"], args["qnorm"], args["kmax"],
-                      args["eligible"], args["bmax"], None)
+                      args["eligible"], args["bmax"], args["kmean"], None)
     return st, L.fsa_last_error().decode()
 
 
 def _attn(info, **kw):
     args = dict(row_ptr=FAKE, col_idx=FAKE, q=FAKE, k=FAKE * 4096, v=FAKE * 8192, o=FAKE * 16384,
-                qnorm=FAKE, kmax=FAKE, eligible=FAKE, batch=1, heads=2, head_dim=64, scale=0.125,
-                head_offset=0, head_count=0)
+                qnorm=FAKE, kmax=FAKE, eligible=FAKE, kmean=0, batch=1, heads=2, head_dim=64,
+                scale=0.125, head_offset=0, head_count=0)
     args.update(kw)
     L = fsa.lib()
     st = L.fsa_attention(ctypes.byref(info) if info is not None else None,
                          args["row_ptr"], args["col_idx"], args["q"], args["k"], args["v"],
-                         args["o"], args["qnorm"], args["kmax"], args["eligible"], args["batch"],
+                         args["o"], args["qnorm"], args["kmax"], args["eligible"], args["kmean"],
+                         args["batch"],
                          args["heads"], args["head_dim"], args["scale"], args["head_offset"],
                          args["head_count"], None)
     return st, L.fsa_last_error().decode()
@@ -82,6 +83,7 @@ BAD_COMMON = [
     (dict(qnorm=0), fsa.FSA_ERR_INVALID_ARG),
     (dict(kmax=FAKE + 1), fsa.FSA_ERR_INVALID_ARG),
     (dict(eligible=0), fsa.FSA_ERR_INVALID_ARG),
+    (dict(kmean=FAKE + 2), fsa.FSA_ERR_INVALID_ARG),     # kmean is optional, but aligned if given
 ]
 
 

@@ -34,10 +34,12 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _run(wl, q, k, v, bq=0, bk=0, bound_limit=0.0, head_offset=0, head_count=0, out=None):
+def _run(wl, q, k, v, bq=0, bk=0, bound_limit=0.0, head_offset=0, head_count=0, out=None,
+         center=False):
     fsa = _fsa()
     dplan = fsa.DevicePlan(wl.frames, wl.tokens_per_frame, wl.window, wl.ref_frame, bq, bk)
-    o, b = fsa.forward(dplan, q, k, v, wl.scale, bound_limit, head_offset, head_count, out=out)
+    o, b = fsa.forward(dplan, q, k, v, wl.scale, bound_limit, head_offset, head_count, out=out,
+                       center=center)
     torch.cuda.synchronize()
     return o, b, dplan
 
@@ -54,13 +56,22 @@ def _assert_close(got, ref, what):
     assert r <= REL_L2, (what, r)
 
 
-def _check_bounds(wl, qc, kc, b, dplan, bq, bk, bound_limit=0.0):
-    qnorm, kmax, eligible, bmax = (t.cpu().numpy() for t in b)
+def _check_bounds(wl, qc, kc, b, dplan, bq, bk, bound_limit=0.0, center=False):
+    qnorm, kmax, eligible, bmax = (t.cpu().numpy() for t in b[:4])
     ref = oracle.bounds(synthetic.to_f64(qc), synthetic.to_f64(kc), *_oracle_args(wl),
-                        dplan.info.block_q, dplan.info.block_k, bound_limit)
+                        dplan.info.block_q, dplan.info.block_k, bound_limit, center=center)
     np.testing.assert_allclose(qnorm, ref["qnorm"], rtol=BOUND_RTOL, atol=0)
-    np.testing.assert_allclose(kmax, ref["kmax"], rtol=BOUND_RTOL, atol=0)
-    np.testing.assert_allclose(bmax, ref["bmax"], rtol=BOUND_RTOL, atol=0)
+    if center:
+        # fp32 sums of N keys: error well under 1e-6 of the largest key entry
+        kmean = b[4].cpu().numpy()
+        scale_k = float(np.abs(synthetic.to_f64(kc)).max())
+        np.testing.assert_allclose(kmean, ref["kmean"], rtol=0, atol=1e-6 * scale_k)
+        # the centred norms inherit that error as an absolute one
+        np.testing.assert_allclose(kmax, ref["kmax"], rtol=BOUND_RTOL, atol=2e-6 * scale_k)
+    else:
+        assert b[4] is None
+        np.testing.assert_allclose(kmax, ref["kmax"], rtol=BOUND_RTOL, atol=0)
+    np.testing.assert_allclose(bmax, ref["bmax"], rtol=BOUND_RTOL if not center else 1e-4, atol=0)
     limit = oracle.effective_bound_limit(bound_limit)
     tie = np.abs(ref["bmax"] - limit) <= 1e-4 * limit
     assert np.all((eligible == ref["eligible"]) | tie)
@@ -99,8 +110,86 @@ def test_small_parity(case):
     _assert_close(synthetic.to_f64(o2), ref, name + " (online)")
 
 
+# ----------------------------------------------------------------- key mean-centring
+CENTRED = [
+    # name, B, H, D, F, T, w, r, bq, bk: one key chunk per head (N <= 2D), several
+    # chunks with a ragged last one, D = 64, and a multi-tile query block
+    ("c_t16_pair", 1, 1, 128, 2, 16, 0, 0, 16, 16),
+    ("c_t240_w1", 1, 2, 128, 3, 240, 1, 0, 240, 80),
+    ("c_t144_d64_b2", 2, 2, 64, 4, 144, 1, 2, 144, 48),
+    ("c_t48_w0_rlast", 2, 3, 128, 4, 48, 0, 3, 48, 16),
+    ("c_t1200_small", 1, 2, 128, 3, 1200, 1, 0, 240, 80),
+]
+
+
+@pytest.mark.parametrize("case", CENTRED, ids=[c[0] for c in CENTRED])
+def test_centred_parity(case):
+    """Keys sharing a 40-long offset: the plain bound is too loose (every head
+    falls back), the centred one is tight (every head takes the bound path),
+    and both outputs match the oracle."""
+    name, bsz, heads, d, frames, t, w, r, bq, bk = case
+    wl = synthetic.Workload(name, bsz, heads, d, frames, t, w, r, dist="key_offset", seed=len(name))
+    _say(f"case {name}: B={bsz} H={heads} D={d} F={frames} T={t} w={w} r={r} bq={bq} bk={bk} centred")
+    qc, kc, vc = synthetic.make_inputs(wl)
+    q, k, v = (x.cuda() for x in (qc, kc, vc))
+    ref = oracle.attention(*(synthetic.to_f64(x) for x in (qc, kc, vc)), *_oracle_args(wl))
+    o, b, dplan = _run(wl, q, k, v, bq, bk, center=True)
+    rb = _check_bounds(wl, qc, kc, b, dplan, bq, bk, center=True)
+    assert np.all(rb["eligible"] == 1)
+    _assert_close(synthetic.to_f64(o), ref, name + " (centred)")
+    o0, b0, _ = _run(wl, q, k, v, bq, bk)
+    rb0 = _check_bounds(wl, qc, kc, b0, dplan, bq, bk)
+    assert np.all(rb0["eligible"] == 0)
+    _assert_close(synthetic.to_f64(o0), ref, name + " (plain)")
+
+
+def test_centred_on_zero_mean_keys_matches_plain():
+    """On N(0,1) keys the centred path gives the same output within tolerance,
+    and both runs are bitwise repeatable."""
+    wl = synthetic.Workload("c_plain", 1, 2, 128, 3, 240, 1, 1, seed=11)
+    qc, kc, vc = synthetic.make_inputs(wl)
+    q, k, v = (x.cuda() for x in (qc, kc, vc))
+    o1, b1, dplan = _run(wl, q, k, v, center=True)
+    o2, b2, _ = _run(wl, q, k, v, center=True)
+    assert torch.equal(o1, o2) and torch.equal(b1[4], b2[4])
+    _check_bounds(wl, qc, kc, b1, dplan, 0, 0, center=True)
+    ref = oracle.attention(*(synthetic.to_f64(x) for x in (qc, kc, vc)), *_oracle_args(wl))
+    _assert_close(synthetic.to_f64(o1), ref, "centred on zero-mean keys")
+
+
+def test_centred_head_range_and_grouping():
+    """Centred calls on a head range write only that range (kmean included),
+    and per-group calls equal the ungrouped call bitwise."""
+    wl = synthetic.Workload("c_hr", 2, 5, 128, 3, 240, 1, 2, dist="key_offset", seed=4)
+    qc, kc, vc = synthetic.make_inputs(wl)
+    q, k, v = (x.cuda() for x in (qc, kc, vc))
+    fsa = _fsa()
+    dplan = fsa.DevicePlan(wl.frames, wl.tokens_per_frame, wl.window, wl.ref_frame)
+    full_o, full_b, _ = _run(wl, q, k, v, center=True)
+    sentinel = torch.full_like(q, 7.0)
+    qn = torch.full((2, 5, wl.seq_len), -1.0, device="cuda")
+    km = torch.full((2, 5, dplan.info.n_kblocks), -1.0, device="cuda")
+    el = torch.full((2, 5), -3, dtype=torch.int32, device="cuda")
+    bm = torch.full((2, 5), -1.0, device="cuda")
+    mu = torch.full((2, 5, 128), -5.0, device="cuda")
+    fsa.bounds(dplan, q, k, wl.scale, 0.0, 1, 3, qn, km, el, bm, kmean=mu)
+    fsa.attention(dplan, q, k, v, qn, km, el, wl.scale, 1, 3, out=sentinel, kmean=mu)
+    torch.cuda.synchronize()
+    for h in (0, 4):
+        assert torch.all(sentinel[:, h] == 7.0) and torch.all(mu[:, h] == -5.0)
+        assert torch.all(qn[:, h] == -1.0) and torch.all(km[:, h] == -1.0)
+        assert torch.all(el[:, h] == -3) and torch.all(bm[:, h] == -1.0)
+    for h0 in (0, 4):
+        fsa.bounds(dplan, q, k, wl.scale, 0.0, h0, 1, qn, km, el, bm, kmean=mu)
+        fsa.attention(dplan, q, k, v, qn, km, el, wl.scale, h0, 1, out=sentinel, kmean=mu)
+    torch.cuda.synchronize()
+    assert torch.equal(sentinel, full_o)
+    for x, y in zip((qn, km, el, bm, mu), full_b):
+        assert torch.equal(x, y)
+
+
 # ----------------------------------------------------------------- full-size workloads
-FULL = ["tiny", "sr720", "sr1080", "bound_stress", "dense"]
+FULL = ["tiny", "sr720", "sr1080", "bound_stress", "dense", "key_offset"]
 _cache = {}
 
 
@@ -118,21 +207,22 @@ def test_full_parity(name):
     wl, qc, kc, vc = _full(name)
     _say(f"workload {name}: N={wl.seq_len} H={wl.heads} D={wl.head_dim}")
     q, k, v = (x.cuda() for x in (qc, kc, vc))
-    o, b, dplan = _run(wl, q, k, v)
-    ref_b = _check_bounds(wl, qc, kc, b, dplan, 0, 0)
-    eligible = b[2].cpu().numpy()
-    if name == "bound_stress":
-        assert np.all(eligible == 0)
-    else:
-        assert np.all(eligible == 1)
-    assert torch.isfinite(o).all().item()
     rows = synthetic.sample_rows(wl, 256 if wl.seq_len > 1000 else 400)
     ref = oracle.attention_rows(synthetic.to_f64(qc), synthetic.to_f64(kc), synthetic.to_f64(vc),
                                 rows, *_oracle_args(wl))
-    oc = o.cpu()
-    got = np.stack([synthetic.to_f64(oc[bb, hh, ii]) for bb, hh, ii in rows])
-    _assert_close(got, ref, name)
-    del ref_b
+    # the key-offset workload needs centring for the bound path; run it both ways
+    for center in ((False, True) if name == "key_offset" else (False,)):
+        o, b, dplan = _run(wl, q, k, v, center=center)
+        _check_bounds(wl, qc, kc, b, dplan, 0, 0, center=center)
+        eligible = b[2].cpu().numpy()
+        if name == "bound_stress" or (name == "key_offset" and not center):
+            assert np.all(eligible == 0)
+        else:
+            assert np.all(eligible == 1)
+        assert torch.isfinite(o).all().item()
+        oc = o.cpu()
+        got = np.stack([synthetic.to_f64(oc[bb, hh, ii]) for bb, hh, ii in rows])
+        _assert_close(got, ref, name + (" (centred)" if center else ""))
 
 
 def test_deterministic_and_grouping_bitwise():
@@ -145,7 +235,7 @@ def test_deterministic_and_grouping_bitwise():
     o2, _, _ = _run(wl, q, k, v)
     assert torch.equal(o1, o2)
     og = torch.full_like(q, float("nan"))
-    qn, km, el, bm = b1
+    qn, km, el, bm = b1[:4]
     streams = [torch.cuda.Stream() for _ in range(4)]
     start = torch.cuda.Event()
     start.record()
@@ -156,11 +246,11 @@ def test_deterministic_and_grouping_bitwise():
     torch.cuda.synchronize()
     assert torch.equal(og, o1)
     # grouped bounds match ungrouped bounds too
-    b2 = [torch.zeros_like(x) for x in b1]
+    b2 = [torch.zeros_like(x) for x in b1[:4]]
     for gi in range(4):
         fsa.bounds(dplan, q, k, wl.scale, 0.0, 2 * gi, 2, *b2)
     torch.cuda.synchronize()
-    for x, y in zip(b1, b2):
+    for x, y in zip(b1[:4], b2):
         assert torch.equal(x, y)
 
 
