@@ -203,6 +203,7 @@ def main():
     if args.center:
         bounds_bytes += bsz * heads * n * d * 2 + 4 * bsz * heads * d
     eligible = el.cpu().numpy()
+    traffic_key = wl.name + ("+center" if args.center else "")
 
     line = {
         "metric": METRIC,
@@ -232,7 +233,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic("fsa_attention", wl.name),
+            "traffic": measured_traffic("fsa_attention", traffic_key),
             "mean_ms": round(attn_mean, 5),
             "median_ms": round(float(np.median(attn_ms)), 5),
             "p10_ms": round(float(np.percentile(attn_ms, 10)), 5),
@@ -246,7 +247,7 @@ def main():
             "input_copies": len(inputs),
             "peak_gbps": PEAK_HBM_GBPS,
             "algorithmic_bytes": bounds_bytes,
-            "traffic": measured_traffic("fsa_bounds_norms", wl.name),
+            "traffic": measured_traffic("fsa_bounds_norms", traffic_key),
         },
     }
     if not args.no_cpu_baseline:

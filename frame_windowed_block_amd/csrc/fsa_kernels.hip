@@ -752,7 +752,8 @@ struct AttnKernel {
 
     // This wavefront's tile: rows row0 .. row0 + nvalid - 1 (nvalid 16 or 32)
     // for NG = 1; NG = 0 stages K/V with the others and meets every barrier.
-    template <int NG>
+    // CENTRED: the bounds were taken over centred keys; mu is the head's key mean.
+    template <int NG, bool CENTRED>
     static __device__ __forceinline__ void tile(const AttnParams &p, char *smem, int64_t head_row0, int32_t row0,
                                                 int nvalid, const uint16_t *kh, const uint16_t *vh, int32_t e0,
                                                 int32_t e1, int32_t nquart, bool online, float mk,
@@ -772,7 +773,7 @@ struct AttnKernel {
             for (int dt = 0; dt < G::DT; ++dt) rw.acc[dt] = f32x16{};
             if (!online) {
                 float shift = p.qnorm[head_row0 + row] * mk;
-                if (mu) {
+                if constexpr (CENTRED) {
                     // centred keys: s_ij = scale q_i.mu + scale q_i.(k_j - mu), and the
                     // bound covers the second term; add this row's q_i.mu. Each half of
                     // the wavefront holds half of the row's columns.
@@ -827,6 +828,7 @@ struct AttnKernel {
         }
     }
 
+    template <bool CENTRED>
     static __device__ void run(const AttnParams &p) {
         extern __shared__ __attribute__((aligned(16))) char smem[];
         float *red = reinterpret_cast<float *>(smem + 2 * G::STAGE);   // stage buffer 2 is free until the walk
@@ -848,7 +850,7 @@ struct AttnKernel {
         const int32_t e1 = __builtin_amdgcn_readfirstlane(p.row_ptr[qb + 1]);
         const int32_t nquart = (e1 - e0) * (p.block_k / 16);
         const bool online = __builtin_amdgcn_readfirstlane(p.eligible[hb]) == 0;
-        const float *mu = p.kmean ? p.kmean + hb * D : nullptr;
+        const float *mu = CENTRED ? p.kmean + hb * D : nullptr;
 
         // bound path: largest key norm over the row's active key blocks
         float mk = 0.0f;
@@ -870,18 +872,20 @@ struct AttnKernel {
             const int32_t row0 = qb * p.block_q + 32 * my;
             const int nvalid = p.block_q - 32 * my < 32 ? p.block_q - 32 * my : 32;
             if (my < ntiles)
-                tile<1>(p, smem, head_row0, row0, nvalid, kh, vh, e0, e1, nquart, online, mk, mu);
+                tile<1, CENTRED>(p, smem, head_row0, row0, nvalid, kh, vh, e0, e1, nquart, online, mk, mu);
             else
-                tile<0>(p, smem, head_row0, row0, nvalid, kh, vh, e0, e1, nquart, online, mk, mu);
+                tile<0, CENTRED>(p, smem, head_row0, row0, nvalid, kh, vh, e0, e1, nquart, online, mk, mu);
             if (t0 + NW < ntiles) lds_barrier();     // LDS reused by the next pass
         }
     }
 };
 
-template <int D>
+// One instantiation per head dim, and per centring: the row shift of the
+// centred one also adds q_i.mean, the plain one keeps the prologue lean.
+template <int D, bool CENTRED>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 attention_kernel(AttnParams p) {
-    AttnKernel<D>::run(p);
+    AttnKernel<D>::template run<CENTRED>(p);
 }
 
 }  // namespace
@@ -980,10 +984,10 @@ int launch_bounds(const BoundsLaunch &a) {
 // ids XCD-first and returns for ids past the work), dynamic LDS for the three
 // stage buffers. The LDS size needs the function attribute, set once per
 // device.
-template <int D>
+template <int D, bool CENTRED>
 int launch_cfg(const AttnParams &p, hipStream_t stream) {
     using K = AttnKernel<D>;
-    auto fn = attention_kernel<D>;
+    auto fn = attention_kernel<D, CENTRED>;
     static std::atomic<uint64_t> attr_done{0};     // one bit per device
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
@@ -1028,8 +1032,8 @@ int launch_attention(const AttentionLaunch &a) {
     p.n_kb = pl.n_kblocks;
     p.c = a.scale * kLog2e;
     hipStream_t stream = static_cast<hipStream_t>(a.stream);
-    if (a.head_dim == 128) return launch_cfg<128>(p, stream);
-    return launch_cfg<64>(p, stream);
+    if (a.head_dim == 128) return a.kmean ? launch_cfg<128, true>(p, stream) : launch_cfg<128, false>(p, stream);
+    return a.kmean ? launch_cfg<64, true>(p, stream) : launch_cfg<64, false>(p, stream);
 }
 
 }  // namespace fsa
