@@ -13,6 +13,9 @@ Sources (the pages reporting the HeyGen / Google Cloud Avatar IV port):
 * [vi:Softmax] same page, section "Giải phóng Softmax" and Fig. 4.
 * [vi:Coll]    same page, section "Ẩn đi các tập lệnh tập thể (Collective)" (head
                groups keep the token order, so each group sees the ungrouped mask).
+* [vi:Layout]  same page, section "Bố cục là ABI" and Fig. 5 (normalisation,
+               rotary embedding, projection and head packing fused into one
+               kernel that writes the layout its consumer reads).
 * [uk:Mask], [uk:Softmax]  bib.com.ua, "HeyGen прискорила Avatar IV на TPU у
                1,86 раза", sections "Маску sparse attention прибрали
                конструктивно" and "Як розірвали послідовний ланцюг softmax"
@@ -369,6 +372,66 @@ def row_bound_by_frames(q, k, frames: int, tokens_per_frame: int, window: int,
 
 
 # --------------------------------------------------------------------------
+# Fused pre-attention [vi:Layout]
+# --------------------------------------------------------------------------
+DEFAULT_RMS_EPS = 1e-6
+DEFAULT_ROPE_BASE = 10000.0
+
+
+def rms_norm(x, gain, eps: float = DEFAULT_RMS_EPS) -> np.ndarray:
+    """x / sqrt(mean over channels of x^2 + eps) * gain, fp64. x: [..., C], gain: [C]."""
+    x = _f64(x)
+    r = 1.0 / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+    return x * r * _f64(gain)
+
+
+def rope_frequencies(head_dim: int, base: float = DEFAULT_ROPE_BASE) -> np.ndarray:
+    """Angular frequency of rotation pair j (j < D/2): base^(-2j/D)."""
+    j = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(float(base), -2.0 * j / head_dim)
+
+
+def rope(t, base: float = DEFAULT_ROPE_BASE) -> np.ndarray:
+    """Rotary position embedding of t: [B, H, N, D], position = token index n.
+
+    Pair j couples features j and j + D/2 and turns them by the angle n * w_j:
+    out_j = t_j cos - t_{j+D/2} sin, out_{j+D/2} = t_{j+D/2} cos + t_j sin."""
+    t = _f64(t)
+    n, d = t.shape[-2], t.shape[-1]
+    ang = np.arange(n, dtype=np.float64)[:, None] * rope_frequencies(d, base)[None, :]   # [N, D/2]
+    c, s = np.cos(ang), np.sin(ang)
+    lo, hi = t[..., : d // 2], t[..., d // 2:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+
+
+def pre_attention(x, gain, w_qkv, heads: int, head_dim: int, eps: float = DEFAULT_RMS_EPS,
+                  rope_base: float = DEFAULT_ROPE_BASE):
+    """The chain that produces the attention inputs, as one function [vi:Layout]:
+    normalisation, projection, rotary embedding and head packing.
+
+    x: [B, N, C] token activations (frame-major tokens); gain: [C];
+    w_qkv: [3 H D, C], a linear layer's weight (output features by input
+    channels): rows 0 .. HD-1 make q, then k, then v; within each, head h owns
+    rows h D .. h D + D - 1. Readings (the page lists the four steps only):
+    RMS normalisation with a per-channel gain, no projection bias, rotary
+    embedding on q and k (not v) at position n = the token's index in its
+    sequence, pairs (j, j + D/2), base 10000.
+
+    Returns q, k, v, each fp64 [B, H, N, D] (the layout the attention reads).
+    """
+    xn = rms_norm(x, gain, eps)                                   # [B, N, C]
+    y = xn @ _f64(w_qkv).T                                        # [B, N, 3 H D]
+    bsz, n, _ = y.shape
+    y = y.reshape(bsz, n, 3, heads, head_dim).transpose(2, 0, 3, 1, 4)   # [3, B, H, N, D]
+    return rope(y[0], rope_base), rope(y[1], rope_base), y[2].copy()
+
+
+def pre_attention_flops(batch: int, seq_len: int, channels: int, heads: int, head_dim: int) -> int:
+    """Algorithmic FLOPs of the projection: 2 C per output feature."""
+    return 2 * batch * seq_len * channels * 3 * heads * head_dim
+
+
+# --------------------------------------------------------------------------
 # Work counts (used for throughput figures)
 # --------------------------------------------------------------------------
 def active_pairs(frames: int, tokens_per_frame: int, window: int, ref_frame: int) -> int:
@@ -399,4 +462,6 @@ __all__ = [
     "attention_bound_shift", "aligned_block_sizes", "auto_block_sizes", "block_classes",
     "check_plan_args", "plan", "effective_bound_limit", "bounds", "row_bound_by_frames",
     "active_pairs", "active_flops", "max_abs_and_rel_l2",
+    "DEFAULT_RMS_EPS", "DEFAULT_ROPE_BASE", "rms_norm", "rope_frequencies", "rope", "pre_attention",
+    "pre_attention_flops",
 ]

@@ -379,8 +379,98 @@ def check_centering(orc):
         np.testing.assert_allclose(c0[key], p0[key], rtol=1e-12, atol=1e-13)
 
 
+# ---------------------------------------------------------------- pre-attention
+def brute_pre_attention(x, gain, w, heads, head_dim, eps, base):
+    """RMS norm, projection, rotary embedding and head packing with Python loops."""
+    bsz, n, c = x.shape
+    out = [np.zeros((bsz, heads, n, head_dim)) for _ in range(3)]
+    half = head_dim // 2
+    for b in range(bsz):
+        for t in range(n):
+            ms = sum(x[b, t, i] ** 2 for i in range(c)) / c
+            xn = [x[b, t, i] / math.sqrt(ms + eps) * gain[i] for i in range(c)]
+            y = [sum(w[o, i] * xn[i] for i in range(c)) for o in range(3 * heads * head_dim)]
+            for part in range(3):
+                for h in range(heads):
+                    row = y[(part * heads + h) * head_dim:(part * heads + h + 1) * head_dim]
+                    for j in range(head_dim):
+                        out[part][b, h, t, j] = row[j]
+                    if part == 2:
+                        continue
+                    for j in range(half):
+                        a = t * base ** (-2.0 * j / head_dim)
+                        lo, hi = row[j], row[j + half]
+                        out[part][b, h, t, j] = lo * math.cos(a) - hi * math.sin(a)
+                        out[part][b, h, t, j + half] = hi * math.cos(a) + lo * math.sin(a)
+    return out
+
+
+def check_pre_attention(orc):
+    """The fused pre-attention chain [vi:Layout]: brute force, a hand-derived
+    rotary embedding, head packing by construction, and the invariances of the
+    normalisation and of the rotation."""
+    # brute force on tiny shapes
+    for seed, (bsz, n, c, heads, d, eps, base) in enumerate(
+            [(1, 3, 4, 1, 2, 1e-6, 10000.0), (2, 4, 6, 2, 4, 1e-3, 100.0), (1, 5, 8, 1, 8, 0.0, 10000.0)]):
+        x = _rand((bsz, n, c), 300 + seed)
+        gain = 0.5 + np.abs(_rand((c,), 310 + seed))
+        w = _rand((3 * heads * d, c), 320 + seed)
+        want = brute_pre_attention(x, gain, w, heads, d, eps, base)
+        got = orc.pre_attention(x, gain, w, heads, d, eps, base)
+        for a, b in zip(got, want):
+            np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    # rotary embedding of hand-derived cases (D = 4, position 2)
+    g = _load("rope_d4_p2.json")
+    t = np.zeros((1, 1, 3, 4))
+    for case in g["cases"]:
+        t[0, 0, 2] = case["in"]
+        np.testing.assert_allclose(orc.rope(t, g["base"])[0, 0, 2], case["out"], rtol=0, atol=2e-9)
+    # head packing: constant tokens, W row o = (o + 1) e_0, one token (no rotation)
+    heads, d, c = 3, 4, 5
+    w = np.zeros((3 * heads * d, c))
+    w[:, 0] = np.arange(1, 3 * heads * d + 1)
+    q, k, v = orc.pre_attention(np.ones((2, 1, c)), np.ones(c), w, heads, d, 0.0)
+    for part, t in enumerate((q, k, v)):
+        for h in range(heads):
+            np.testing.assert_allclose(t[:, h, 0], np.broadcast_to(
+                part * heads * d + h * d + 1 + np.arange(d), (2, d)), rtol=0, atol=1e-12)
+    # normalisation: identity projection shows x / rms(x) * gain; scale-free at eps = 0
+    heads, d = 2, 4
+    c = heads * d
+    x = _rand((1, 6, c), 330)
+    gain = 0.5 + np.abs(_rand((c,), 331))
+    w = np.concatenate([np.eye(c)] * 3)
+    _, _, v = orc.pre_attention(x, gain, w, heads, d, 0.0)
+    vv = v.transpose(0, 2, 1, 3).reshape(1, 6, c)
+    np.testing.assert_allclose((vv / gain) ** 2 @ np.ones(c), c, rtol=1e-12)
+    np.testing.assert_allclose(vv / gain * np.sqrt((x * x).mean(-1, keepdims=True)), x, rtol=0, atol=1e-12)
+    for a, b in zip(orc.pre_attention(7.5 * x, gain, w, heads, d, 0.0),
+                    orc.pre_attention(x, gain, w, heads, d, 0.0)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    # rotation: pair norms are kept, and with the same token at every position
+    # q_n . k_m depends on n - m only
+    w = _rand((3 * heads * d, c), 332)
+    row = _rand((1, 1, c), 333)
+    xs = np.repeat(row, 7, axis=1)
+    q, k, v = orc.pre_attention(xs, np.ones(c), w, heads, d, 1e-6)
+    half = d // 2
+    pn = q[..., :half] ** 2 + q[..., half:] ** 2
+    np.testing.assert_allclose(pn, np.broadcast_to(pn[:, :, :1], pn.shape), rtol=1e-12)
+    for h in range(heads):
+        dots = q[0, h] @ k[0, h].T
+        for s_ in range(-6, 7):
+            diag = np.diagonal(dots, offset=s_)
+            np.testing.assert_allclose(diag, diag[0], rtol=0, atol=1e-11)
+    # v is not rotated: the same token gives the same v at every position
+    np.testing.assert_allclose(v, np.broadcast_to(v[:, :, :1], v.shape), rtol=0, atol=1e-12)
+    # q at position 0 is the plain projection of the normalised token
+    xn = row[0, 0] / np.sqrt((row[0, 0] ** 2).mean() + 1e-6)
+    np.testing.assert_allclose(q[0, :, 0].reshape(-1), w[:heads * d] @ xn, rtol=0, atol=1e-12)
+
+
 ALL_CHECKS = [
     check_golden_attention, check_golden_plans, check_brute_force, check_weights,
     check_dense_limit, check_closed_forms, check_bound_shift_exact, check_cauchy_schwarz,
     check_plan_closed_form, check_plan_negative_control, check_invariances, check_centering,
+    check_pre_attention,
 ]

@@ -14,6 +14,8 @@ import oracle
 from oracle import fsa_oracle as fo
 from tests import oracle_pins
 
+fo.ROPE_ORIG = fo.rope
+
 
 def _namespace(**overrides):
     ns = types.SimpleNamespace(**{name: getattr(oracle, name) for name in oracle.__all__})
@@ -123,6 +125,67 @@ def _query_mean(res, q, k, scale, mask_args):
     res["kmean"] = q.mean(axis=2)
 
 
+def _rope_interleaved(t, base=10000.0):
+    t = np.asarray(t, dtype=np.float64)
+    n, d = t.shape[-2], t.shape[-1]
+    ang = np.arange(n)[:, None] * fo.rope_frequencies(d, base)[None, :]
+    c, s_ = np.cos(ang), np.sin(ang)
+    out = t.copy()
+    out[..., 0::2] = t[..., 0::2] * c - t[..., 1::2] * s_
+    out[..., 1::2] = t[..., 1::2] * c + t[..., 0::2] * s_
+    return out
+
+
+def _rope_sign(t, base=10000.0):
+    t = np.asarray(t, dtype=np.float64)
+    d = t.shape[-1]
+    flip = np.ones(d)
+    flip[d // 2:] = -1.0
+    return fo.ROPE_ORIG(t * flip, base) * flip
+
+
+def _rope_from_one(t, base=10000.0):
+    t = np.asarray(t, dtype=np.float64)
+    n, d = t.shape[-2], t.shape[-1]
+    ang = (1.0 + np.arange(n))[:, None] * fo.rope_frequencies(d, base)[None, :]
+    c, s_ = np.cos(ang), np.sin(ang)
+    lo, hi = t[..., : d // 2], t[..., d // 2:]
+    return np.concatenate([lo * c - hi * s_, hi * c + lo * s_], axis=-1)
+
+
+def _pre_rope_v(x, gain, w, heads, d, eps=1e-6, base=10000.0):
+    q, k, v = oracle.pre_attention(x, gain, w, heads, d, eps, base)
+    return q, k, fo.rope(v, base)
+
+
+def _pre_heads_swapped(x, gain, w, heads, d, eps=1e-6, base=10000.0):
+    xn = fo.rms_norm(x, gain, eps)
+    y = xn @ np.asarray(w, dtype=np.float64).T
+    bsz, n, _ = y.shape
+    y = y.reshape(bsz, n, 3, d, heads).transpose(2, 0, 4, 1, 3)
+    return fo.rope(y[0], base), fo.rope(y[1], base), y[2].copy()
+
+
+def _pre_qk_swapped(x, gain, w, heads, d, eps=1e-6, base=10000.0):
+    q, k, v = oracle.pre_attention(x, gain, w, heads, d, eps, base)
+    return k, q, v
+
+
+def _rms_over_tokens(x, gain, eps=1e-6):
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt((x * x).mean(axis=-2, keepdims=True) + eps) * np.asarray(gain)
+
+
+def _rms_no_gain(x, gain, eps=1e-6):
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+
+
+def _rms_no_sqrt(x, gain, eps=1e-6):
+    x = np.asarray(x, dtype=np.float64)
+    return x / ((x * x).mean(axis=-1, keepdims=True) + eps) * np.asarray(gain)
+
+
 def _plan_descending(*args, **kw):
     info, row_ptr, col_idx = oracle.plan(*args, **kw)
     col = col_idx.copy()
@@ -155,6 +218,15 @@ MUTANTS = {
     "centred shift over uncentred key norms": dict(ns={"bounds": _centred(_uncentred_norms)}),
     "key mean taken per key block": dict(ns={"bounds": _centred(_block_mean)}),
     "query mean used as the key mean": dict(ns={"bounds": _centred(_query_mean)}),
+    "rotary pairs interleaved": dict(module={"rope": _rope_interleaved}),
+    "rotary sine with the wrong sign": dict(module={"rope": _rope_sign}),
+    "rotary positions counted from one": dict(module={"rope": _rope_from_one}),
+    "rotary embedding applied to v": dict(ns={"pre_attention": _pre_rope_v}),
+    "head and feature axes swapped in packing": dict(ns={"pre_attention": _pre_heads_swapped}),
+    "q and k outputs swapped": dict(ns={"pre_attention": _pre_qk_swapped}),
+    "rms taken over tokens": dict(module={"rms_norm": _rms_over_tokens}),
+    "norm gain dropped": dict(module={"rms_norm": _rms_no_gain}),
+    "rms without the square root": dict(module={"rms_norm": _rms_no_sqrt}),
     "key blocks listed descending": dict(ns={"plan": _plan_descending}),
     "query and key block sizes swapped": dict(ns={"plan": _plan_swapped_sizes}),
 }
