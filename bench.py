@@ -20,6 +20,9 @@ between two device synchronisations. Prints ONE JSON line:
   FETCH_SIZE / WRITE_SIZE passes (profiles/traffic.json), reported only while
   the kernel source still matches the one those counters were taken on.
 
+--kernel pre_attention times fsa_pre_attention alone (workload pre720 unless
+another pre-attention workload is named) and prints its own JSON line.
+
 --center runs fsa_bounds with key mean-centring (and fsa_attention with the
 resulting key mean); the default is off, as on the headline workload.
 
@@ -41,17 +44,18 @@ METRIC = "effective TFLOP/s on active blocks + % of bf16 MFMA peak, 25k-token SR
 PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "frame_windowed_block_amd", "csrc", "fsa_kernels.hip")
+PRE_SOURCE = os.path.join(ROOT, "frame_windowed_block_amd", "csrc", "fsa_preattn.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel: str, workload: str, source: str = KERNEL_SOURCE):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     passes (copy-calibrated), or None when they were taken on other kernel source."""
     import hashlib
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)[kernel][workload]
-        with open(KERNEL_SOURCE, "rb") as fh:
+        with open(source, "rb") as fh:
             sha = hashlib.sha256(fh.read()).hexdigest()
     except (OSError, KeyError, ValueError):
         return None
@@ -74,6 +78,9 @@ def parse():
                     help="copies of q, k, v that consecutive steps rotate over")
     ap.add_argument("--center", action="store_true",
                     help="mean-centre the keys in fsa_bounds (key_offset workload)")
+    ap.add_argument("--kernel", default="attention", choices=["attention", "pre_attention"],
+                    help="pre_attention: time fsa_pre_attention alone on a pre-attention workload "
+                         "(default pre720) and print its own JSON line")
     return ap.parse_args()
 
 
@@ -101,12 +108,111 @@ def cpu_baseline(wl, qc, kc, vc, heads: int):
                       f"({flops:.3e} active FLOPs; dense fp64 masked softmax), {dt:.2f} s wall"}
 
 
+def bench_pre_attention(args):
+    """fsa_pre_attention alone: normalisation + q/k/v projection + rotary
+    embedding + head packing, inputs resident in HBM (rotating over copies of
+    x), one JSON line."""
+    import numpy as np
+    import torch
+
+    import frame_windowed_block_amd as fsa
+    import oracle
+    import synthetic
+
+    name = args.workload if args.workload in synthetic.PRE_WORKLOADS else "pre720"
+    wl = synthetic.PRE_WORKLOADS[name]
+    x, gain, w = synthetic.make_pre_inputs(wl)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    xs = [x.to(dev) for _ in range(max(1, args.copies))]
+    # the norm gain is folded into the weight once, as a model load would do
+    wd = (w.float() * gain[None, :]).to(torch.bfloat16).to(dev)
+    shape = (wl.batch, wl.heads, wl.seq_len, wl.head_dim)
+    outs = [torch.empty(shape, dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        fsa.pre_attention(xs[i % len(xs)], wd, wl.heads, wl.head_dim, q=outs[0], k=outs[1],
+                          v=outs[2], stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    total_ms = t0.elapsed_time(t1)
+    flops = oracle.pre_attention_flops(wl.batch, wl.seq_len, wl.channels, wl.heads, wl.head_dim)
+    kbytes = 2 * wl.batch * wl.seq_len * wl.channels + \
+        2 * 3 * wl.heads * wl.head_dim * wl.channels + 3 * 2 * wl.batch * wl.heads * wl.seq_len * wl.head_dim
+    med = float(np.median(ms))
+    value = flops * args.steps / (total_ms * 1e-3) / 1e12
+    line = {
+        "metric": "fused pre-attention (norm + qkv projection + rotary + head packing) TFLOP/s",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.seq_len,
+                   "channels": wl.channels, "heads": wl.heads, "head_dim": wl.head_dim,
+                   "flops": flops, "algorithmic_bytes": kbytes, "input_copies": len(xs)},
+        "roofline": {
+            "kernel": "fsa_pre_attention", "bound": "mfma",
+            "achieved": round(flops / (float(ms.mean()) * 1e-3) / 1e12, 3),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(flops / (float(ms.mean()) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic("fsa_pre_attention", wl.name, PRE_SOURCE),
+            "mean_ms": round(float(ms.mean()), 5), "median_ms": round(med, 5),
+            "hbm_gbps_algorithmic": round(kbytes / (med * 1e-3) / 1e9, 1),
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_pre(wl, x, gain, w)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_pre(wl, x, gain, w, tokens: int = 1 << 30):
+    """Time the fp64 oracle on (at most) the first `tokens` tokens of batch item 0
+    (by default the whole sequence: the oracle's projection is one BLAS call)."""
+    import numpy as np
+
+    import oracle
+    import synthetic
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:                                  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    xs = synthetic.to_f64(x[:1, :tokens])
+    t0 = time.perf_counter()
+    out = oracle.pre_attention(xs, gain.double().numpy(), synthetic.to_f64(w), wl.heads, wl.head_dim)
+    dt = time.perf_counter() - t0
+    assert all(np.isfinite(o).all() for o in out)
+    flops = oracle.pre_attention_flops(1, xs.shape[1], wl.channels, wl.heads, wl.head_dim)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"batch 0, tokens 0..{xs.shape[1] - 1} of {wl.seq_len} ({flops:.3e} FLOPs, "
+                      f"fp64), {dt:.2f} s wall"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
               "head across GPUs but no multi-GPU run is built.", file=sys.stderr)
         sys.exit(2)
+
+    if args.kernel == "pre_attention" and not args.copy_calibration:
+        bench_pre_attention(args)
+        return
 
     import numpy as np
     import torch

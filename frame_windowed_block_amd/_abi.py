@@ -75,6 +75,9 @@ def lib() -> ctypes.CDLL:
         L.fsa_attention.restype = ctypes.c_int
         L.fsa_attention.argtypes = [ctypes.POINTER(PlanInfo), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _P, _I32, _I32, _I32, _F32, _I32, _I32, _P]
+        L.fsa_pre_attention.restype = ctypes.c_int
+        L.fsa_pre_attention.argtypes = [_P, _P, _I32, _I32, _I32, _I32, _I32, _F32, _F32,
+                                        _P, _P, _P, _P]
         _lib = L
     return _lib
 
@@ -210,3 +213,27 @@ def forward(dplan: DevicePlan, q, k, v, scale: float, bound_limit: float = 0.0,
     o = attention(dplan, q, k, v, b[0], b[1], b[2], scale, head_offset, head_count,
                   out=out, stream=stream, kmean=b[4])
     return o, b
+
+
+def pre_attention(x, w_qkv, heads: int, head_dim: int, eps: float = 1e-6,
+                  rope_base: float = 10000.0, q=None, k=None, v=None, stream=None):
+    """fsa_pre_attention: x bf16 [B, N, C], w_qkv bf16 [3 H D, C] (a norm gain
+    already folded in) -> (q, k, v), each bf16 [B, H, N, D]."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or x.dim() != 3 or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("x must be a contiguous bf16 CUDA tensor [B, N, C]")
+    bsz, n, c = x.shape
+    if (w_qkv.dtype != torch.bfloat16 or tuple(w_qkv.shape) != (3 * heads * head_dim, c)
+            or not w_qkv.is_contiguous()):
+        raise ValueError("w_qkv must be a contiguous bf16 tensor [3 H D, C]")
+    outs = []
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t is None:
+            t = torch.empty((bsz, heads, n, head_dim), dtype=torch.bfloat16, device=x.device)
+        else:
+            _check_qkv(name, t, (bsz, heads, n, head_dim))
+        outs.append(t)
+    _check(lib().fsa_pre_attention(_ptr(x), _ptr(w_qkv), bsz, n, c, heads, head_dim,
+                                   float(eps), float(rope_base), _ptr(outs[0]), _ptr(outs[1]),
+                                   _ptr(outs[2]), _stream_handle(stream)))
+    return tuple(outs)

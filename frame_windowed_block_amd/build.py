@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfsa.so")
-SOURCES = ["fsa_plan.cpp", "fsa_api.cpp", "fsa_kernels.hip"]
+SOURCES = ["fsa_plan.cpp", "fsa_api.cpp", "fsa_kernels.hip", "fsa_preattn.hip"]
 ARCH = "gfx950"
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -142,4 +142,60 @@ fsa_status fsa_attention(const fsa_plan_info *plan, const int32_t *d_row_ptr, co
     return FSA_OK;
 }
 
+fsa_status fsa_pre_attention(const void *x, const void *w_qkv, int32_t batch,
+                             int32_t seq_len, int32_t channels, int32_t heads, int32_t head_dim, float eps,
+                             float rope_base, void *q, void *k, void *v, void *stream) {
+    using namespace fsa;
+    clear_error();
+    if (batch < 0) return fail(FSA_ERR_INVALID_ARG, "batch = %d, must be >= 0", batch);
+    if (seq_len < 0) return fail(FSA_ERR_INVALID_ARG, "seq_len = %d, must be >= 0", seq_len);
+    if (heads < 0) return fail(FSA_ERR_INVALID_ARG, "heads = %d, must be >= 0", heads);
+    if (channels <= 0 || channels % 32)
+        return fail(FSA_ERR_UNSUPPORTED, "channels = %d; must be a positive multiple of 32", channels);
+    if (head_dim <= 0) return fail(FSA_ERR_INVALID_ARG, "head_dim = %d, must be > 0", head_dim);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(FSA_ERR_UNSUPPORTED, "head_dim = %d; built for 64 and 128", head_dim);
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(FSA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (!(rope_base > 0.0f) || !std::isfinite(rope_base))
+        return fail(FSA_ERR_INVALID_ARG, "rope_base must be finite and > 0");
+    if (int64_t(3) * heads * head_dim > (int64_t(1) << 30))
+        return fail(FSA_ERR_INVALID_ARG, "3 * heads * head_dim overflows");
+    const int64_t tokens = int64_t(batch) * seq_len;
+    if (batch > 0 && tokens / batch != seq_len) return fail(FSA_ERR_INVALID_ARG, "tensor size overflows");
+    if (tokens > (int64_t(1) << 40) || tokens * channels > (int64_t(1) << 60) ||
+        tokens * heads * head_dim > (int64_t(1) << 60))
+        return fail(FSA_ERR_INVALID_ARG, "tensor size overflows");
+    if (tokens == 0 || heads == 0) return FSA_OK;
+    FSA_TRY(check_vec16(x, "x"));
+    FSA_TRY(check_vec16(w_qkv, "w_qkv"));
+    FSA_TRY(check_vec16(q, "q"));
+    FSA_TRY(check_vec16(k, "k"));
+    FSA_TRY(check_vec16(v, "v"));
+    if (((tokens + 255) / 256) * ((int64_t(3) * heads * head_dim + 255) / 256) + 8 > kMaxWorkgroups)
+        return fail(FSA_ERR_UNSUPPORTED, "problem needs more workgroups than one launch holds");
+    // the outputs must not overlap each other or an input
+    struct Span { uintptr_t lo, hi; };
+    const int64_t out_bytes = tokens * heads * head_dim * 2;
+    const Span outs[3] = {{reinterpret_cast<uintptr_t>(q), reinterpret_cast<uintptr_t>(q) + uintptr_t(out_bytes)},
+                          {reinterpret_cast<uintptr_t>(k), reinterpret_cast<uintptr_t>(k) + uintptr_t(out_bytes)},
+                          {reinterpret_cast<uintptr_t>(v), reinterpret_cast<uintptr_t>(v) + uintptr_t(out_bytes)}};
+    const Span ins[2] = {
+        {reinterpret_cast<uintptr_t>(x), reinterpret_cast<uintptr_t>(x) + uintptr_t(tokens * channels * 2)},
+        {reinterpret_cast<uintptr_t>(w_qkv),
+         reinterpret_cast<uintptr_t>(w_qkv) + uintptr_t(int64_t(3) * heads * head_dim * channels * 2)}};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 2; ++j)
+            if (outs[i].lo < ins[j].hi && ins[j].lo < outs[i].hi)
+                return fail(FSA_ERR_INVALID_ARG, "an output overlaps an input");
+        for (int j = i + 1; j < 3; ++j)
+            if (outs[i].lo < outs[j].hi && outs[j].lo < outs[i].hi)
+                return fail(FSA_ERR_INVALID_ARG, "q, k and v must not overlap");
+    }
+    PreAttentionLaunch a{x, w_qkv, batch, seq_len, channels, heads, head_dim, eps, rope_base,
+                         q, k, v, stream};
+    const int err = launch_pre_attention(a);
+    if (err) return fail(FSA_ERR_HIP, "fsa_pre_attention launch failed: %s", hip_error_text(err));
+    return FSA_OK;
+}
+
 }  // extern "C"

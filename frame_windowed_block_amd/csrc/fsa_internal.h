@@ -46,10 +46,20 @@ struct AttentionLaunch {
     void *stream;
 };
 
-// Kernel launchers (fsa_kernels.hip). They assume validated arguments and
+struct PreAttentionLaunch {
+    const void *x;
+    const void *w_qkv;
+    int32_t batch, seq_len, channels, heads, head_dim;
+    float eps, rope_base;
+    void *q, *k, *v;
+    void *stream;
+};
+
+// Kernel launchers (fsa_kernels.hip, fsa_preattn.hip). They assume validated arguments and
 // return 0 or the HIP runtime's error code; hip_error_text names a code.
 int launch_bounds(const BoundsLaunch &a);
 int launch_attention(const AttentionLaunch &a);
+int launch_pre_attention(const PreAttentionLaunch &a);
 const char *hip_error_text(int code);
 
 // Largest number of workgroups one launch may use (grid x times 256 threads

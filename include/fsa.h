@@ -26,6 +26,10 @@
  *                  (section "Giải phóng Softmax", Fig. 4). A head range lets a
  *                  caller run independent head groups that each see exactly the
  *                  ungrouped mask (section "Ẩn đi các tập lệnh tập thể (Collective)").
+ *   fsa_pre_attention  the chain that produces q, k, v (normalisation,
+ *                  projection, rotary embedding, head packing) as one kernel
+ *                  writing the [B, H, N, D] layout the two calls above read
+ *                  (section "Bố cục là ABI", Fig. 5).
  *
  * Notation: B batch, H heads, F frames, T tokens per frame, N = F*T tokens,
  * D head dim, w window half-width (frames), r reference frame, bq / bk query /
@@ -178,6 +182,42 @@ fsa_status fsa_attention(const fsa_plan_info *plan, const int32_t *d_row_ptr, co
                          const float *qnorm, const float *kmax, const int32_t *eligible,
                          const float *kmean, int32_t batch, int32_t heads, int32_t head_dim, float scale,
                          int32_t head_offset, int32_t head_count, void *stream);
+
+/*
+ * fsa_pre_attention - the chain that makes the attention inputs, fused into
+ * one kernel whose outputs are already in the layout fsa_bounds and
+ * fsa_attention read (section "Bố cục là ABI", Fig. 5: normalisation, rotary
+ * embedding, projection and head packing in one kernel, no repacking copies).
+ * Device, asynchronous on `stream`.
+ *
+ * For token (b, n) with activations x_t = x[b, n, :]:
+ *   r_t = 1 / sqrt(mean_c x_t[c]^2 + eps)               (RMS normalisation)
+ *   y_t = r_t * (x_t . w_qkv^T)                         (projection, no bias)
+ *   q[b,h,n,:] = rot(y_t[h D .. h D + D - 1], n)
+ *   k[b,h,n,:] = rot(y_t[H D + h D .. ], n)
+ *   v[b,h,n,:] = y_t[2 H D + h D .. ]                   (not rotated)
+ * rot(u, n) turns each feature pair (j, j + D/2), j < D/2, by the angle
+ * n * rope_base^(-2 j / D): out_j = u_j cos - u_{j+D/2} sin,
+ * out_{j+D/2} = u_{j+D/2} cos + u_j sin (n = the token's index in its sequence).
+ * A normalisation gain g is folded into the weight beforehand,
+ * w_qkv[o, c] = W[o, c] * g[c] rounded to bf16: in exact arithmetic
+ * (r x * g) . W^T = r (x . (W diag g)^T).
+ * Accumulation is fp32 (bf16 MFMA); r_t and the rotation are applied in fp32;
+ * outputs are rounded to bf16 (RNE).
+ *
+ * x:       device bf16 [B, N, C] (row-major, channels fastest).
+ * w_qkv:   device bf16 [3 H D, C], a linear layer's weight (output features
+ *          by input channels): q rows of head h at h D, then k, then v.
+ * q, k, v: device bf16 [B, H, N, D] outputs; they must not overlap each other
+ *          or an input. All five pointers 16-byte aligned.
+ * channels C: a positive multiple of 32 (else FSA_ERR_UNSUPPORTED).
+ * head_dim D: 64 or 128 (else FSA_ERR_UNSUPPORTED).
+ * eps >= 0 and rope_base > 0, both finite (typical: 1e-6 and 10000).
+ * B == 0, N == 0 or H == 0 is a no-op returning FSA_OK. Errors as above.
+ */
+fsa_status fsa_pre_attention(const void *x, const void *w_qkv, int32_t batch, int32_t seq_len,
+                             int32_t channels, int32_t heads, int32_t head_dim, float eps,
+                             float rope_base, void *q, void *k, void *v, void *stream);
 
 /* Static English text for a status code (never NULL). */
 const char *fsa_status_string(fsa_status status);

@@ -391,21 +391,23 @@ def rope_frequencies(head_dim: int, base: float = DEFAULT_ROPE_BASE) -> np.ndarr
     return np.power(float(base), -2.0 * j / head_dim)
 
 
-def rope(t, base: float = DEFAULT_ROPE_BASE) -> np.ndarray:
-    """Rotary position embedding of t: [B, H, N, D], position = token index n.
+def rope(t, base: float = DEFAULT_ROPE_BASE, positions=None) -> np.ndarray:
+    """Rotary position embedding of t: [B, H, N, D], position = token index n
+    (or ``positions[n]`` when given, for a subset of a sequence's tokens).
 
-    Pair j couples features j and j + D/2 and turns them by the angle n * w_j:
+    Pair j couples features j and j + D/2 and turns them by the angle p * w_j:
     out_j = t_j cos - t_{j+D/2} sin, out_{j+D/2} = t_{j+D/2} cos + t_j sin."""
     t = _f64(t)
     n, d = t.shape[-2], t.shape[-1]
-    ang = np.arange(n, dtype=np.float64)[:, None] * rope_frequencies(d, base)[None, :]   # [N, D/2]
+    pos = np.arange(n, dtype=np.float64) if positions is None else _f64(positions)
+    ang = pos[:, None] * rope_frequencies(d, base)[None, :]                          # [N, D/2]
     c, s = np.cos(ang), np.sin(ang)
     lo, hi = t[..., : d // 2], t[..., d // 2:]
     return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
 
 
 def pre_attention(x, gain, w_qkv, heads: int, head_dim: int, eps: float = DEFAULT_RMS_EPS,
-                  rope_base: float = DEFAULT_ROPE_BASE):
+                  rope_base: float = DEFAULT_ROPE_BASE, positions=None):
     """The chain that produces the attention inputs, as one function [vi:Layout]:
     normalisation, projection, rotary embedding and head packing.
 
@@ -417,13 +419,16 @@ def pre_attention(x, gain, w_qkv, heads: int, head_dim: int, eps: float = DEFAUL
     embedding on q and k (not v) at position n = the token's index in its
     sequence, pairs (j, j + D/2), base 10000.
 
+    ``positions`` (optional, [N]) gives each token's index in its sequence when
+    x holds only some of the sequence's tokens.
+
     Returns q, k, v, each fp64 [B, H, N, D] (the layout the attention reads).
     """
     xn = rms_norm(x, gain, eps)                                   # [B, N, C]
     y = xn @ _f64(w_qkv).T                                        # [B, N, 3 H D]
     bsz, n, _ = y.shape
     y = y.reshape(bsz, n, 3, heads, head_dim).transpose(2, 0, 3, 1, 4)   # [3, B, H, N, D]
-    return rope(y[0], rope_base), rope(y[1], rope_base), y[2].copy()
+    return rope(y[0], rope_base, positions), rope(y[1], rope_base, positions), y[2].copy()
 
 
 def pre_attention_flops(batch: int, seq_len: int, channels: int, heads: int, head_dim: int) -> int:

@@ -116,6 +116,39 @@ def make_inputs(wl: Workload, device: str = "cpu"):
     return tuple(out)
 
 
+# Inputs of the fused pre-attention chain (article section "Bố cục là ABI"):
+# token activations x [B, N, C], a per-channel norm gain and the q/k/v
+# projection weight [3 H D, C]. The article gives no model width; C = H D.
+@dataclasses.dataclass(frozen=True)
+class PreWorkload:
+    name: str
+    batch: int
+    seq_len: int
+    channels: int
+    heads: int
+    head_dim: int
+    seed: int = 0
+
+
+PRE_WORKLOADS = {
+    "pre_tiny": PreWorkload("pre_tiny", 1, 400, 128, 2, 64),
+    "pre720": PreWorkload("pre720", 1, 25200, 1024, 8, 128),
+}
+
+
+def make_pre_inputs(wl: PreWorkload):
+    """x ~ N(0, 1) as bf16 [B, N, C]; gain = 1 + 0.1 N(0, 1) as fp32 [C];
+    w ~ N(0, 1/C) as bf16 [3 H D, C] (so the projections have unit variance).
+    One ``torch.Generator('cpu')`` seeded with ``wl.seed`` draws x, gain, w in
+    that order."""
+    g = torch.Generator("cpu").manual_seed(wl.seed)
+    x = torch.randn((wl.batch, wl.seq_len, wl.channels), generator=g, dtype=torch.float32)
+    gain = 1.0 + 0.1 * torch.randn((wl.channels,), generator=g, dtype=torch.float32)
+    w = torch.randn((3 * wl.heads * wl.head_dim, wl.channels), generator=g, dtype=torch.float32)
+    w /= math.sqrt(wl.channels)
+    return x.to(torch.bfloat16), gain, w.to(torch.bfloat16)
+
+
 def to_f64(t: torch.Tensor):
     """Exact fp64 numpy copy of a bf16 tensor (every bf16 value is an fp64 value)."""
     return t.detach().to("cpu").to(torch.float64).numpy()

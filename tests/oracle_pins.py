@@ -463,6 +463,20 @@ def check_pre_attention(orc):
             np.testing.assert_allclose(diag, diag[0], rtol=0, atol=1e-11)
     # v is not rotated: the same token gives the same v at every position
     np.testing.assert_allclose(v, np.broadcast_to(v[:, :, :1], v.shape), rtol=0, atol=1e-12)
+    # a norm gain folded into the weight gives the same outputs (the form the
+    # kernel takes): (r x * g) W^T = r x (W diag g)^T
+    x = _rand((2, 5, c), 335)
+    gain = 0.5 + np.abs(_rand((c,), 336))
+    for a, b in zip(orc.pre_attention(x, gain, w, heads, d, 1e-6),
+                    orc.pre_attention(x, np.ones(c), w * gain[None, :], heads, d, 1e-6)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    # a subset of tokens with their positions gives the same rows
+    x = _rand((2, 9, c), 334)
+    full = orc.pre_attention(x, gain, w, heads, d, 1e-6)
+    sel = np.array([8, 0, 5])
+    part = orc.pre_attention(x[:, sel], gain, w, heads, d, 1e-6, positions=sel)
+    for a, b in zip(part, full):
+        np.testing.assert_allclose(a, b[:, :, sel], rtol=0, atol=1e-12)
     # q at position 0 is the plain projection of the normalised token
     xn = row[0, 0] / np.sqrt((row[0, 0] ** 2).mean() + 1e-6)
     np.testing.assert_allclose(q[0, :, 0].reshape(-1), w[:heads * d] @ xn, rtol=0, atol=1e-12)

@@ -143,3 +143,45 @@ def test_binding_raises():
     with pytest.raises(fsa.FsaError) as ei:
         fsa.plan(5, 72, 1, 0)
     assert ei.value.status == fsa.FSA_ERR_UNALIGNED
+
+
+def _pre(**kw):
+    args = dict(x=FAKE, w=FAKE * 3, batch=1, seq_len=16, channels=64, heads=2,
+                head_dim=64, eps=1e-6, base=10000.0, q=FAKE * 4096, k=FAKE * 8192, v=FAKE * 16384)
+    args.update(kw)
+    L = fsa.lib()
+    st = L.fsa_pre_attention(args["x"], args["w"], args["batch"], args["seq_len"],
+                             args["channels"], args["heads"], args["head_dim"], args["eps"],
+                             args["base"], args["q"], args["k"], args["v"], None)
+    return st, L.fsa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(batch=-1), fsa.FSA_ERR_INVALID_ARG),
+    (dict(seq_len=-1), fsa.FSA_ERR_INVALID_ARG),
+    (dict(heads=-1), fsa.FSA_ERR_INVALID_ARG),
+    (dict(channels=48), fsa.FSA_ERR_UNSUPPORTED),
+    (dict(channels=0), fsa.FSA_ERR_UNSUPPORTED),
+    (dict(head_dim=96), fsa.FSA_ERR_UNSUPPORTED),
+    (dict(head_dim=0), fsa.FSA_ERR_INVALID_ARG),
+    (dict(eps=-1.0), fsa.FSA_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), fsa.FSA_ERR_INVALID_ARG),
+    (dict(base=0.0), fsa.FSA_ERR_INVALID_ARG),
+    (dict(base=float("inf")), fsa.FSA_ERR_INVALID_ARG),
+    (dict(x=0), fsa.FSA_ERR_INVALID_ARG),
+    (dict(x=FAKE + 8), fsa.FSA_ERR_INVALID_ARG),
+    (dict(w=0), fsa.FSA_ERR_INVALID_ARG),
+    (dict(q=FAKE * 4096 + 2), fsa.FSA_ERR_INVALID_ARG),
+    (dict(v=0), fsa.FSA_ERR_INVALID_ARG),
+    (dict(q=FAKE), fsa.FSA_ERR_INVALID_ARG),                    # overlaps x
+    (dict(k=FAKE * 4096 + 16), fsa.FSA_ERR_INVALID_ARG),        # overlaps q
+])
+def test_pre_attention_rejects(kw, want):
+    st, msg = _pre(**kw)
+    assert st == want and msg
+
+
+def test_pre_attention_empty_is_noop():
+    assert _pre(batch=0, x=0, q=0)[0] == fsa.FSA_OK
+    assert _pre(seq_len=0, x=0)[0] == fsa.FSA_OK
+    assert _pre(heads=0, w=0)[0] == fsa.FSA_OK

@@ -1,0 +1,170 @@
+"""Fused pre-attention kernel against the fp64 oracle, through the C ABI.
+
+The kernel takes the projection weight with the norm gain folded in,
+w' = bf16(w * gain); the oracle is given the same w' and a unit gain, so both
+sides compute the same function. Error bound checked on every output element
+(derived from the arithmetic): the MFMA accumulates exact bf16 products in
+fp32, 1/rms and the rotation are applied in fp32 with the hardware sine/cosine
+(angles reduced in fp32, at most ~41 revolutions), and the output is rounded
+to bf16 (<= 2^-8 relative). With A = r * sum_c |x_c w'_oc| (summed over both
+members of a rotation pair for q and k), every element must satisfy
+    |got - ref| <= 2^-8 |ref| + 2^-12 A,
+where 2^-12 A covers fp32 accumulation and the sine/cosine error. The whole
+tensor must also meet rel-L2 <= 5e-3.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 5e-3
+
+
+def _fsa():
+    import frame_windowed_block_amd as fsa
+    fsa.lib()
+    return fsa
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _fold(w, gain):
+    """The kernel's weight: the norm gain folded in, rounded to bf16."""
+    return (w.float() * gain[None, :]).to(torch.bfloat16)
+
+
+def _abs_bound(x, w, heads, d, eps):
+    """A per output element (see the module docstring), as [3][B, H, N, D]."""
+    x = np.asarray(x, dtype=np.float64)
+    r = 1.0 / np.sqrt((x * x).mean(-1, keepdims=True) + eps)
+    a = r * (np.abs(x) @ np.abs(np.asarray(w, dtype=np.float64)).T)            # [B, N, 3HD]
+    bsz, n, _ = a.shape
+    a = a.reshape(bsz, n, 3, heads, d).transpose(2, 0, 3, 1, 4)
+    out = []
+    for part in range(3):
+        t = a[part]
+        if part < 2:
+            pair = t[..., : d // 2] + t[..., d // 2:]
+            t = np.concatenate([pair, pair], axis=-1)
+        out.append(t)
+    return out
+
+
+def _check(got, ref, bound, what):
+    got = synthetic.to_f64(got)
+    err = np.abs(got - ref)
+    lim = 2.0 ** -8 * np.abs(ref) + 2.0 ** -12 * bound
+    _, rel = oracle.max_abs_and_rel_l2(got, ref)
+    worst = float((err / lim).max()) if err.size else 0.0
+    _say(f"{what}: rel_l2={rel:.3e} worst err/bound={worst:.3f}")
+    assert np.isfinite(got).all(), what
+    assert np.all(err <= lim), (what, worst)
+    assert rel <= REL_L2, (what, rel)
+
+
+CASES = [
+    # name, B, N, C, H, D
+    ("d64_ragged", 2, 300, 96, 2, 64),
+    ("d128_257", 1, 257, 128, 1, 128),
+    ("short_16", 1, 16, 32, 3, 128),
+    ("seq_40_b7", 7, 40, 160, 1, 128),
+    ("b2_513_c256", 2, 513, 256, 2, 128),
+    ("tile_exact", 1, 512, 64, 2, 64),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_pre_attention_parity(case):
+    name, bsz, n, c, heads, d = case
+    wl = synthetic.PreWorkload(name, bsz, n, c, heads, d, seed=len(name))
+    _say(f"case {name}: B={bsz} N={n} C={c} H={heads} D={d}")
+    x, gain, w = synthetic.make_pre_inputs(wl)
+    wg = _fold(w, gain)
+    fsa = _fsa()
+    q, k, v = fsa.pre_attention(x.cuda(), wg.cuda(), heads, d)
+    torch.cuda.synchronize()
+    xf, wf = synthetic.to_f64(x), synthetic.to_f64(wg)
+    ref = oracle.pre_attention(xf, np.ones(c), wf, heads, d)
+    bound = _abs_bound(xf, wf, heads, d, oracle.DEFAULT_RMS_EPS)
+    for got, want, bd, tag in zip((q, k, v), ref, bound, "qkv"):
+        _check(got, want, bd, f"{name} {tag}")
+
+
+def test_pre_attention_options_and_determinism():
+    """Other eps and rotary base values, and bitwise-repeatable outputs."""
+    wl = synthetic.PreWorkload("opt", 1, 200, 64, 2, 128, seed=9)
+    x, gain, w = synthetic.make_pre_inputs(wl)
+    wg = _fold(w, gain)
+    fsa = _fsa()
+    xd, wd = x.cuda(), wg.cuda()
+    xf, wf = synthetic.to_f64(x), synthetic.to_f64(wg)
+    for eps, base in ((0.5, 500.0), (0.0, 1e6)):
+        outs = fsa.pre_attention(xd, wd, 2, 128, eps, base)
+        again = fsa.pre_attention(xd, wd, 2, 128, eps, base)
+        torch.cuda.synchronize()
+        for a, b in zip(outs, again):
+            assert torch.equal(a, b)
+        ref = oracle.pre_attention(xf, np.ones(64), wf, 2, 128, eps, base)
+        bound = _abs_bound(xf, wf, 2, 128, eps)
+        for got, want, bd, tag in zip(outs, ref, bound, "qkv"):
+            _check(got, want, bd, f"eps={eps} base={base} {tag}")
+
+
+def test_pre_attention_full_size_sampled():
+    """The 720p-shaped workload (25,200 tokens, C = 1024, 8 heads of 128):
+    sampled tokens against the oracle (which takes their positions)."""
+    wl = synthetic.PRE_WORKLOADS["pre720"]
+    _say(f"workload pre720: N={wl.seq_len} C={wl.channels} H={wl.heads} D={wl.head_dim}")
+    x, gain, w = synthetic.make_pre_inputs(wl)
+    wg = _fold(w, gain)
+    fsa = _fsa()
+    q, k, v = fsa.pre_attention(x.cuda(), wg.cuda(), wl.heads, wl.head_dim)
+    torch.cuda.synchronize()
+    g = torch.Generator("cpu").manual_seed(3)
+    sel = torch.randint(0, wl.seq_len, (96,), generator=g).tolist()
+    sel = np.array(sorted(set(sel) | {0, 255, 256, 257, 511, 512, wl.seq_len - 1}))
+    xf = synthetic.to_f64(x[:, sel])
+    wf = synthetic.to_f64(wg)
+    ref = oracle.pre_attention(xf, np.ones(wl.channels), wf, wl.heads, wl.head_dim, positions=sel)
+    bound = _abs_bound(xf, wf, wl.heads, wl.head_dim, oracle.DEFAULT_RMS_EPS)
+    for got, want, bd, tag in zip((q, k, v), ref, bound, "qkv"):
+        _check(got[:, :, sel].cpu(), want, bd, f"pre720 {tag}")
+        assert torch.isfinite(got).all().item()
+
+
+def test_pre_attention_feeds_attention():
+    """x -> fused pre-attention -> bounds -> attention, against the oracle's
+    chain: pre-attention in fp64, its q, k, v rounded to bf16 (the hand-off
+    format both sides share), then masked attention in fp64."""
+    frames, t, w_, r = 3, 240, 1, 0
+    wl = synthetic.PreWorkload("chain", 1, frames * t, 256, 2, 128, seed=5)
+    x, gain, w = synthetic.make_pre_inputs(wl)
+    wg = _fold(w, gain)
+    fsa = _fsa()
+    q, k, v = fsa.pre_attention(x.cuda(), wg.cuda(), 2, 128)
+    dplan = fsa.DevicePlan(frames, t, w_, r)
+    scale = float(torch.tensor(128 ** -0.5, dtype=torch.float32))
+    o, b = fsa.forward(dplan, q, k, v, scale)
+    torch.cuda.synchronize()
+    # the attention step on the kernel's own q, k, v: the spec bar
+    ref = oracle.attention(*(synthetic.to_f64(a) for a in (q, k, v)), frames, t, w_, r, scale)
+    m, rel = oracle.max_abs_and_rel_l2(synthetic.to_f64(o), ref)
+    _say(f"chain (attention on the fused q, k, v): eligible={b[2].cpu().tolist()} "
+         f"max_abs={m:.3e} rel_l2={rel:.3e}")
+    assert m <= 1e-2 and rel <= 5e-3
+    # end to end against the fp64 chain: the attention floor plus the
+    # pre-attention error carried through the softmax; held to 1e-2 rel-L2
+    qr, kr, vr = oracle.pre_attention(synthetic.to_f64(x), np.ones(256), synthetic.to_f64(wg), 2, 128)
+    ref = oracle.attention(qr, kr, vr, frames, t, w_, r, scale)
+    m, rel = oracle.max_abs_and_rel_l2(synthetic.to_f64(o), ref)
+    _say(f"chain end to end: max_abs={m:.3e} rel_l2={rel:.3e}")
+    assert m <= 1e-2 and rel <= 1e-2

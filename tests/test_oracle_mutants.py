@@ -125,10 +125,11 @@ def _query_mean(res, q, k, scale, mask_args):
     res["kmean"] = q.mean(axis=2)
 
 
-def _rope_interleaved(t, base=10000.0):
+def _rope_interleaved(t, base=10000.0, positions=None):
     t = np.asarray(t, dtype=np.float64)
     n, d = t.shape[-2], t.shape[-1]
-    ang = np.arange(n)[:, None] * fo.rope_frequencies(d, base)[None, :]
+    pos = np.arange(n) if positions is None else np.asarray(positions, dtype=np.float64)
+    ang = pos[:, None] * fo.rope_frequencies(d, base)[None, :]
     c, s_ = np.cos(ang), np.sin(ang)
     out = t.copy()
     out[..., 0::2] = t[..., 0::2] * c - t[..., 1::2] * s_
@@ -136,38 +137,39 @@ def _rope_interleaved(t, base=10000.0):
     return out
 
 
-def _rope_sign(t, base=10000.0):
+def _rope_sign(t, base=10000.0, positions=None):
     t = np.asarray(t, dtype=np.float64)
     d = t.shape[-1]
     flip = np.ones(d)
     flip[d // 2:] = -1.0
-    return fo.ROPE_ORIG(t * flip, base) * flip
+    return fo.ROPE_ORIG(t * flip, base, positions) * flip
 
 
-def _rope_from_one(t, base=10000.0):
+def _rope_from_one(t, base=10000.0, positions=None):
     t = np.asarray(t, dtype=np.float64)
     n, d = t.shape[-2], t.shape[-1]
-    ang = (1.0 + np.arange(n))[:, None] * fo.rope_frequencies(d, base)[None, :]
+    pos = np.arange(n) if positions is None else np.asarray(positions, dtype=np.float64)
+    ang = (1.0 + pos)[:, None] * fo.rope_frequencies(d, base)[None, :]
     c, s_ = np.cos(ang), np.sin(ang)
     lo, hi = t[..., : d // 2], t[..., d // 2:]
     return np.concatenate([lo * c - hi * s_, hi * c + lo * s_], axis=-1)
 
 
-def _pre_rope_v(x, gain, w, heads, d, eps=1e-6, base=10000.0):
-    q, k, v = oracle.pre_attention(x, gain, w, heads, d, eps, base)
-    return q, k, fo.rope(v, base)
+def _pre_rope_v(x, gain, w, heads, d, eps=1e-6, base=10000.0, positions=None):
+    q, k, v = oracle.pre_attention(x, gain, w, heads, d, eps, base, positions)
+    return q, k, fo.rope(v, base, positions)
 
 
-def _pre_heads_swapped(x, gain, w, heads, d, eps=1e-6, base=10000.0):
+def _pre_heads_swapped(x, gain, w, heads, d, eps=1e-6, base=10000.0, positions=None):
     xn = fo.rms_norm(x, gain, eps)
     y = xn @ np.asarray(w, dtype=np.float64).T
     bsz, n, _ = y.shape
     y = y.reshape(bsz, n, 3, d, heads).transpose(2, 0, 4, 1, 3)
-    return fo.rope(y[0], base), fo.rope(y[1], base), y[2].copy()
+    return fo.rope(y[0], base, positions), fo.rope(y[1], base, positions), y[2].copy()
 
 
-def _pre_qk_swapped(x, gain, w, heads, d, eps=1e-6, base=10000.0):
-    q, k, v = oracle.pre_attention(x, gain, w, heads, d, eps, base)
+def _pre_qk_swapped(x, gain, w, heads, d, eps=1e-6, base=10000.0, positions=None):
+    q, k, v = oracle.pre_attention(x, gain, w, heads, d, eps, base, positions)
     return k, q, v
 
 
