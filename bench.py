@@ -21,7 +21,9 @@ between two device synchronisations. Prints ONE JSON line:
   the kernel source still matches the one those counters were taken on.
 
 --kernel pre_attention times fsa_pre_attention alone (workload pre720 unless
-another pre-attention workload is named) and prints its own JSON line.
+another pre-attention workload is named) and prints its own JSON line;
+--kernel chain times x -> fsa_pre_attention -> fsa_bounds -> fsa_attention on
+the 720p shape.
 
 --center runs fsa_bounds with key mean-centring (and fsa_attention with the
 resulting key mean); the default is off, as on the headline workload.
@@ -78,9 +80,10 @@ def parse():
                     help="copies of q, k, v that consecutive steps rotate over")
     ap.add_argument("--center", action="store_true",
                     help="mean-centre the keys in fsa_bounds (key_offset workload)")
-    ap.add_argument("--kernel", default="attention", choices=["attention", "pre_attention"],
+    ap.add_argument("--kernel", default="attention", choices=["attention", "pre_attention", "chain"],
                     help="pre_attention: time fsa_pre_attention alone on a pre-attention workload "
-                         "(default pre720) and print its own JSON line")
+                         "(default pre720) and print its own JSON line; chain: x -> fused "
+                         "pre-attention -> bounds -> attention on the 720p shape, its own JSON line")
     return ap.parse_args()
 
 
@@ -180,6 +183,68 @@ def bench_pre_attention(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_chain(args):
+    """The attention layer's hot path end to end on the 720p shape: x [1, N, C]
+    -> fsa_pre_attention -> fsa_bounds -> fsa_attention, inputs resident in
+    HBM (rotating over copies of x). One JSON line; value = the projection's
+    and the attention's algorithmic FLOPs per second of whole steps."""
+    import torch
+
+    import frame_windowed_block_amd as fsa
+    import oracle
+    import synthetic
+
+    pw = synthetic.PRE_WORKLOADS["pre720"]
+    aw = synthetic.WORKLOADS["sr720"]
+    assert (pw.seq_len, pw.heads, pw.head_dim) == (aw.seq_len, aw.heads, aw.head_dim)
+    x, gain, w = synthetic.make_pre_inputs(pw)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    xs = [x.to(dev) for _ in range(max(1, args.copies))]
+    wd = (w.float() * gain[None, :]).to(torch.bfloat16).to(dev)
+    shape = (pw.batch, pw.heads, pw.seq_len, pw.head_dim)
+    q, k, v, o = (torch.empty(shape, dtype=torch.bfloat16, device=dev) for _ in range(4))
+    dplan = fsa.DevicePlan(aw.frames, aw.tokens_per_frame, aw.window, aw.ref_frame, device=dev)
+    info = dplan.info
+    qn = torch.empty(shape[:3], dtype=torch.float32, device=dev)
+    km = torch.empty((pw.batch, pw.heads, info.n_kblocks), dtype=torch.float32, device=dev)
+    el = torch.empty((pw.batch, pw.heads), dtype=torch.int32, device=dev)
+    bm = torch.empty((pw.batch, pw.heads), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        fsa.pre_attention(xs[i % len(xs)], wd, pw.heads, pw.head_dim, q=q, k=k, v=v, stream=stream)
+        fsa.bounds(dplan, q, k, aw.scale, 0.0, 0, 0, qn, km, el, bm, stream=stream)
+        fsa.attention(dplan, q, k, v, qn, km, el, aw.scale, 0, 0, out=o, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    pre_flops = oracle.pre_attention_flops(pw.batch, pw.seq_len, pw.channels, pw.heads, pw.head_dim)
+    attn_flops = oracle.active_flops(aw.batch, aw.heads, aw.head_dim, aw.frames, aw.tokens_per_frame,
+                                     aw.window, aw.ref_frame)
+    line = {
+        "metric": "attention-layer hot path x -> q,k,v -> o (fused pre-attention + bounds + attention) TFLOP/s",
+        "value": round((pre_flops + attn_flops) / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "pre720 + sr720", "tokens": pw.seq_len, "channels": pw.channels,
+                   "heads": pw.heads, "head_dim": pw.head_dim, "pre_flops": pre_flops,
+                   "attention_flops": attn_flops, "eligible_heads": int(el.sum().item())},
+        "pct_of_peak": round(100.0 * (pre_flops + attn_flops) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline_pre(wl, x, gain, w, tokens: int = 1 << 30):
     """Time the fp64 oracle on (at most) the first `tokens` tokens of batch item 0
     (by default the whole sequence: the oracle's projection is one BLAS call)."""
@@ -212,6 +277,9 @@ def main():
 
     if args.kernel == "pre_attention" and not args.copy_calibration:
         bench_pre_attention(args)
+        return
+    if args.kernel == "chain" and not args.copy_calibration:
+        bench_chain(args)
         return
 
     import numpy as np

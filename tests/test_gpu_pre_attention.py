@@ -141,6 +141,25 @@ def test_pre_attention_full_size_sampled():
         assert torch.isfinite(got).all().item()
 
 
+def test_pre_attention_long_sequence_positions():
+    """Positions up to 2^20: the rotation angles of late tokens come from the
+    fp64 table entry of their tile plus the row offset; sampled tokens near the
+    start, around tile edges and at the very end match the oracle."""
+    n = 1 << 20
+    wl = synthetic.PreWorkload("long", 1, n, 32, 1, 64, seed=21)
+    x, gain, w = synthetic.make_pre_inputs(wl)
+    wg = _fold(w, gain)
+    fsa = _fsa()
+    q, k, v = fsa.pre_attention(x.cuda(), wg.cuda(), 1, 64)
+    torch.cuda.synchronize()
+    sel = np.array([0, 1, 255, 256, 257, 65535, 65536, 300001, n // 2 + 17, n - 257, n - 256, n - 1])
+    xf, wf = synthetic.to_f64(x[:, sel]), synthetic.to_f64(wg)
+    ref = oracle.pre_attention(xf, np.ones(32), wf, 1, 64, positions=sel)
+    bound = _abs_bound(xf, wf, 1, 64, oracle.DEFAULT_RMS_EPS)
+    for got, want, bd, tag in zip((q, k, v), ref, bound, "qkv"):
+        _check(got[:, :, sel].cpu(), want, bd, f"long {tag}")
+
+
 def test_pre_attention_feeds_attention():
     """x -> fused pre-attention -> bounds -> attention, against the oracle's
     chain: pre-attention in fp64, its q, k, v rounded to bf16 (the hand-off
