@@ -25,6 +25,9 @@ another pre-attention workload is named) and prints its own JSON line;
 --kernel chain times x -> fsa_pre_attention -> fsa_bounds -> fsa_attention on
 the 720p shape.
 
+--groups G splits fsa_attention into G head groups on G streams (the grouped
+dense configuration); roofline then covers the span of the grouped launches.
+
 --center runs fsa_bounds with key mean-centring (and fsa_attention with the
 resulting key mean); the default is off, as on the headline workload.
 
@@ -78,6 +81,9 @@ def parse():
                     help="heads of the workload the CPU oracle is timed on")
     ap.add_argument("--copies", type=int, default=3,
                     help="copies of q, k, v that consecutive steps rotate over")
+    ap.add_argument("--groups", type=int, default=1,
+                    help="run fsa_attention as this many head groups on as many streams "
+                         "(roofline then times the span from the bounds to the last group)")
     ap.add_argument("--center", action="store_true",
                     help="mean-centre the keys in fsa_bounds (key_offset workload)")
     ap.add_argument("--kernel", default="attention", choices=["attention", "pre_attention", "chain"],
@@ -322,6 +328,10 @@ def main():
     bm = torch.empty((bsz, heads), dtype=torch.float32, device=dev)
     mu = torch.empty((bsz, heads, d), dtype=torch.float32, device=dev) if args.center else None
     stream = torch.cuda.current_stream()
+    if args.groups > 1 and heads % args.groups:
+        print(f"--groups {args.groups} does not divide {heads} heads", file=sys.stderr)
+        sys.exit(2)
+    group_streams = [torch.cuda.Stream() for _ in range(args.groups)] if args.groups > 1 else []
 
     def step(i, ev=None):
         q, k, v = inputs[i % len(inputs)]
@@ -344,7 +354,22 @@ def main():
         fsa.bounds(dplan, q, k, wl.scale, 0.0, 0, 0, qn, km, el, bm, stream=stream, kmean=mu)
         if ev is not None:
             ev[1].record(stream)
-        fsa.attention(dplan, q, k, v, qn, km, el, wl.scale, 0, 0, out=o, stream=stream, kmean=mu)
+        if args.groups <= 1:
+            fsa.attention(dplan, q, k, v, qn, km, el, wl.scale, 0, 0, out=o, stream=stream, kmean=mu)
+        else:
+            # head groups on their own streams, each waiting for the bounds
+            # (the one-GPU part of head-group pipelining); the step stream
+            # waits for all of them
+            ready = torch.cuda.Event()
+            ready.record(stream)
+            hg = heads // args.groups
+            for g, gs in enumerate(group_streams):
+                gs.wait_event(ready)
+                fsa.attention(dplan, q, k, v, qn, km, el, wl.scale, g * hg, hg, out=o, stream=gs,
+                              kmean=mu)
+                done = torch.cuda.Event()
+                done.record(gs)
+                stream.wait_event(done)
         if ev is not None:
             ev[2].record(stream)
 
@@ -398,6 +423,7 @@ def main():
             "window": wl.window, "ref_frame": wl.ref_frame, "block_q": info0.block_q,
             "block_k": info0.block_k, "nnz": info0.nnz, "active_flops": flops,
             "eligible_heads": int(eligible.sum()), "key_centring": bool(args.center),
+            "head_groups": args.groups,
         },
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {
@@ -407,7 +433,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic("fsa_attention", traffic_key),
+            "traffic": measured_traffic("fsa_attention", traffic_key) if args.groups <= 1 else None,
             "mean_ms": round(attn_mean, 5),
             "median_ms": round(float(np.median(attn_ms)), 5),
             "p10_ms": round(float(np.percentile(attn_ms, 10)), 5),
