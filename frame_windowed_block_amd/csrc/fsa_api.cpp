@@ -39,6 +39,10 @@ fsa_status check_common(const fsa_plan_info *plan, int32_t batch, int32_t heads,
     if (batch > 0 && heads > 0 && elems / batch / heads / plan->seq_len != head_dim)
         return fail(FSA_ERR_INVALID_ARG, "tensor size overflows");
     if (elems > (int64_t(1) << 60)) return fail(FSA_ERR_INVALID_ARG, "tensor size overflows");
+    // the kernels address one head's K / V slab with 32-bit byte offsets
+    if (int64_t(plan->seq_len) * head_dim * 2 >= (int64_t(1) << 31))
+        return fail(FSA_ERR_UNSUPPORTED, "seq_len * head_dim * 2 = %lld bytes per head; must be below 2 GiB",
+                    (long long)(int64_t(plan->seq_len) * head_dim * 2));
     *count = hc;
     *empty = batch == 0 || hc == 0;
     return FSA_OK;

@@ -321,10 +321,14 @@ __global__ __launch_bounds__(256) void bound_reduce_kernel(ReduceParams p) {
     float bound = 0.0f;
     if (qb < p.n_qb) {
         const float *qn = p.qnorm + hb * p.seq_len + int64_t(qb) * p.block_q;
+        // loops unrolled so that each lane's loads are in flight together
+        // (the list entries first, then the key-block maxima they index)
         float qm = 0.0f;
+#pragma unroll 8
         for (int i = sl; i < p.block_q; i += 16) qm = nan_max(qm, qn[i]);
         const int32_t e0 = p.row_ptr[qb], e1 = p.row_ptr[qb + 1];
         float km = 0.0f;
+#pragma unroll 4
         for (int32_t e = e0 + sl; e < e1; e += 16) km = nan_max(km, p.kmax[hb * p.n_kb + p.col_idx[e]]);
 #pragma unroll
         for (int off = 8; off >= 1; off >>= 1) {

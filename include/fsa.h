@@ -170,7 +170,9 @@ fsa_status fsa_bounds(const fsa_plan_info *plan, const int32_t *d_row_ptr, const
  *             scale and head range (only the range is read). kmean must be
  *             NULL exactly when that fsa_bounds call had NULL: centred norms
  *             with an uncentred shift (or the reverse) are not a bound.
- * head_dim:   64 or 128 (else FSA_ERR_UNSUPPORTED).
+ * head_dim:   64 or 128 (else FSA_ERR_UNSUPPORTED). One head's q / k / v slab
+ *             (N * D * 2 bytes) must be below 2 GiB (else FSA_ERR_UNSUPPORTED),
+ *             for fsa_bounds as well.
  * head_offset, head_count: as for fsa_bounds; rows of other heads in o are
  *             not written, so several calls on disjoint head ranges may run
  *             concurrently on different streams.

@@ -185,3 +185,14 @@ def test_pre_attention_empty_is_noop():
     assert _pre(batch=0, x=0, q=0)[0] == fsa.FSA_OK
     assert _pre(seq_len=0, x=0)[0] == fsa.FSA_OK
     assert _pre(heads=0, w=0)[0] == fsa.FSA_OK
+
+
+def test_head_slab_limit():
+    """One head's K / V slab is addressed with 32-bit byte offsets: N * D * 2
+    must stay below 2 GiB (rejected before anything is launched)."""
+    info, _, _ = fsa.plan(8192, 1024, 0, 0)          # N = 2^23 tokens
+    assert info.seq_len == 1 << 23
+    st, msg = _bounds(info, head_dim=128)
+    assert st == fsa.FSA_ERR_UNSUPPORTED and "2 GiB" in msg
+    st, msg = _attn(info, head_dim=128)
+    assert st == fsa.FSA_ERR_UNSUPPORTED and "2 GiB" in msg
