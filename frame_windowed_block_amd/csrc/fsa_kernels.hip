@@ -406,15 +406,11 @@ __device__ __forceinline__ void lds_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Query-block order inside a head: frames from the middle outwards, so the
-// first workgroups of a head share their key window in L2 and the cheaper edge
-// frames (fewer visible frames) run last.
-__device__ __forceinline__ int32_t rank_to_qblock(int32_t rank, int32_t frames, int32_t qpf) {
-    const int32_t fr = rank / qpf, qi = rank % qpf;
-    const int32_t mid = (frames - 1) / 2;
-    const int32_t f = (fr & 1) ? mid + (fr + 1) / 2 : mid - fr / 2;
-    return f * qpf + qi;
-}
+// Query-block order inside a head: the plan's own order (frame by frame). The
+// workgroups an XCD runs at one time then cover a contiguous run of frames,
+// whose key windows overlap in that XCD's L2. (Ordering the frames from the
+// middle outwards balanced no better and shared less.)
+__device__ __forceinline__ int32_t rank_to_qblock(int32_t rank) { return rank; }
 
 // Buffer descriptor over one head's K or V slab (raw, unswizzled, 32-bit data).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t *base, int64_t bytes) {
@@ -844,8 +840,7 @@ struct AttnKernel {
         const int64_t L = (bid & 7) * p.per_xcd + (bid >> 3);
         if (L >= p.total_wg) return;
         const int64_t bh = L / p.n_qb;
-        const int32_t qpf = p.tokens_per_frame / p.block_q;
-        const int32_t qb = rank_to_qblock(int32_t(L % p.n_qb), p.frames, qpf);
+        const int32_t qb = rank_to_qblock(int32_t(L % p.n_qb));
         const int64_t hb = (bh / p.hc) * p.heads + p.h0 + bh % p.hc;
         const int64_t head_row0 = hb * p.seq_len;
         const uint16_t *kh = p.k + head_row0 * D;
