@@ -1,0 +1,31 @@
+"""bench.py's command-line contract on the CPU: one GPU only, and the option
+parser accepts what the measurement docs name (no GPU is touched)."""
+import os
+import subprocess
+import sys
+
+from tests.conftest import ROOT
+
+BENCH = os.path.join(ROOT, "bench.py")
+
+
+def _run(*args):
+    return subprocess.run([sys.executable, BENCH, *args], capture_output=True, text=True, timeout=120,
+                          cwd=ROOT)
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = _run("--gpus", "2", "--steps", "1", "--warmup", "0")
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""                      # no JSON line for a run that did not happen
+
+
+def test_help_lists_the_kernels_and_options():
+    r = _run("--help")
+    assert r.returncode == 0
+    for opt in ("--gpus", "--steps", "--warmup", "--workload", "--no-cpu-baseline", "--center",
+                "--groups", "--kernel", "--copy-calibration"):
+        assert opt in r.stdout, opt
+    for kernel in ("attention", "pre_attention", "chain"):
+        assert kernel in r.stdout, kernel
