@@ -1,8 +1,11 @@
 """HIP path against the fp64 oracle, through the C ABI (needs an MI355X).
 
 Bars: block plans bit-exact (CPU tests), bounds within 1e-5 relative, and
-attention outputs (bf16) within max-abs 1e-2 and relative L2 5e-3 of the
-oracle. Small shapes are compared element by element on every output; the
+attention outputs (bf16) within relative L2 5e-3 of the oracle and, element
+by element, within max-abs 1e-2 or one bf16 step of the reference value where
+that step is larger (|o| >= 2, reached on heavy-tailed inputs whose rows are
+nearly one-hot: there rounding the exact result to bf16 alone can move it by
+more than 1e-2). Small shapes are compared element by element on every output; the
 full-size workloads on seeded samples of rows (the oracle computes those rows
 exactly) plus whole-tensor properties.
 """
@@ -48,11 +51,19 @@ def _oracle_args(wl):
     return (wl.frames, wl.tokens_per_frame, wl.window, wl.ref_frame, wl.scale)
 
 
+def _bf16_step(x):
+    """Spacing of bf16 numbers (8 significant bits) at |x|."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
 def _assert_close(got, ref, what):
     m, r = oracle.max_abs_and_rel_l2(got, ref)
-    _say(f"{what}: max_abs={m:.3e} rel_l2={r:.3e}")
+    bar = np.maximum(MAX_ABS, _bf16_step(ref))
+    excess = float((np.abs(got - ref) - bar).max()) if got.size else 0.0
+    _say(f"{what}: max_abs={m:.3e} rel_l2={r:.3e} worst excess over the bar={excess:.3e}")
     assert np.isfinite(got).all(), what
-    assert m <= MAX_ABS, (what, m)
+    assert excess <= 0.0, (what, m, excess)
     assert r <= REL_L2, (what, r)
 
 
@@ -186,6 +197,50 @@ def test_centred_head_range_and_grouping():
     assert torch.equal(sentinel, full_o)
     for x, y in zip((qn, km, el, bm, mu), full_b):
         assert torch.equal(x, y)
+
+
+# ----------------------------------------------------------------- seeded sweep of small shapes
+def _random_cases(n=24, seed=20261203):
+    """Seeded random small shapes: T a multiple of 16 up to 512, block sizes
+    drawn from the multiples of 16 dividing T, 1-6 frames, window 0-3, any
+    reference frame, D 64 or 128, 1-2 batch items, 1-3 heads, normal or
+    heavy-tailed inputs; N stays <= 1536 so the oracle is quick. This walks
+    the kernel through stage counts of every residue of its 3-way unrolled
+    loop, odd and even 16-key tile counts, query blocks with idle wavefronts
+    and query blocks taking several passes."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        t = 16 * int(rng.integers(1, 33))
+        frames = int(rng.integers(1, 7))
+        if frames * t > 1536:
+            continue
+        divs = [16 * m for m in range(1, t // 16 + 1) if t % (16 * m) == 0]
+        cases.append((f"rnd{len(cases)}", int(rng.integers(1, 3)), int(rng.integers(1, 4)),
+                      int(rng.choice([64, 128])), frames, t, int(rng.integers(0, 4)),
+                      int(rng.integers(0, frames)), int(rng.choice(divs)), int(rng.choice(divs)),
+                      str(rng.choice(["normal", "normal", "bound_stress"]))))
+    return cases
+
+
+RANDOM = _random_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[c[0] for c in RANDOM])
+def test_random_small_parity(case):
+    name, bsz, heads, d, frames, t, w, r, bq, bk, dist = case
+    wl = synthetic.Workload(name, bsz, heads, d, frames, t, w, r, dist=dist, seed=1000 + len(name) + t)
+    _say(f"case {name}: B={bsz} H={heads} D={d} F={frames} T={t} w={w} r={r} bq={bq} bk={bk} {dist}")
+    qc, kc, vc = synthetic.make_inputs(wl)
+    q, k, v = (x.cuda() for x in (qc, kc, vc))
+    o, b, dplan = _run(wl, q, k, v, bq, bk)
+    _check_bounds(wl, qc, kc, b, dplan, bq, bk)
+    ref = oracle.attention(*(synthetic.to_f64(x) for x in (qc, kc, vc)), *_oracle_args(wl))
+    _assert_close(synthetic.to_f64(o), ref, name)
+    if int(name[3:]) % 3 == 0:
+        o2, b2, _ = _run(wl, q, k, v, bq, bk, bound_limit=1e-30)
+        assert int(b2[2].sum()) == 0
+        _assert_close(synthetic.to_f64(o2), ref, name + " (online)")
 
 
 # ----------------------------------------------------------------- full-size workloads
