@@ -99,6 +99,23 @@ def test_pre_attention_parity(case):
         _check(got, want, bd, f"{name} {tag}")
 
 
+def _random_cases(n=12, seed=20261204):
+    """Seeded random shapes: C any multiple of 32 up to 512 (odd multiples end
+    on a half-empty channel stage), N 1..700 (ragged token tiles, one tile
+    crossing into the next sequence), 1-3 batch items, 1-4 heads, D 64 or 128."""
+    rng = np.random.default_rng(seed)
+    return [(f"rnd{i}", int(rng.integers(1, 4)), int(rng.integers(1, 701)), 32 * int(rng.integers(1, 17)),
+             int(rng.integers(1, 5)), int(rng.choice([64, 128]))) for i in range(n)]
+
+
+RANDOM = _random_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[c[0] for c in RANDOM])
+def test_pre_attention_random_parity(case):
+    test_pre_attention_parity(case)
+
+
 def test_pre_attention_options_and_determinism():
     """Other eps and rotary base values, and bitwise-repeatable outputs."""
     wl = synthetic.PreWorkload("opt", 1, 200, 64, 2, 128, seed=9)
