@@ -204,8 +204,12 @@ __global__ __launch_bounds__(256) void norms_kernel(NormsParams p) {
             p.bmax[hb] = 0.0f;
         }
     }
-    const int64_t unit = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    // the key-block units (the longer ones) are dispatched first, so that the
+    // short query units fill in behind them
+    int64_t unit = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (unit >= p.total_units) return;
+    const int64_t k_units = p.total_units - p.q_units;
+    unit = unit < k_units ? p.q_units + unit : unit - k_units;
 
     if (unit < p.q_units) {
         const int64_t units_per_head = (p.seq_len / 16 + QG - 1) / QG;
