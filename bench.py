@@ -71,7 +71,7 @@ def measured_traffic(kernel: str, workload: str, source: str = KERNEL_SOURCE):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="sr720")
     ap.add_argument("--no-cpu-baseline", action="store_true")
