@@ -29,3 +29,15 @@ def test_help_lists_the_kernels_and_options():
         assert opt in r.stdout, opt
     for kernel in ("attention", "pre_attention", "chain"):
         assert kernel in r.stdout, kernel
+
+
+def test_traffic_is_reported_only_for_the_profiled_kernel_source(tmp_path):
+    """roofline.traffic comes from the committed counter passes only while the
+    kernel source is byte-identical to the one they were taken on."""
+    import bench
+    here = bench.measured_traffic("fsa_attention", "sr720")
+    assert here is not None and here > 0         # the committed profile matches the committed kernel
+    edited = tmp_path / "kernel.hip"
+    edited.write_bytes(open(bench.KERNEL_SOURCE, "rb").read() + b"\n// edited\n")
+    assert bench.measured_traffic("fsa_attention", "sr720", str(edited)) is None
+    assert bench.measured_traffic("fsa_attention", "no_such_workload") is None
