@@ -36,7 +36,9 @@
 // The scores of sub-step j + 1 are computed in the same step as the weights
 // and p.v of sub-step j. Heads whose bound is too loose run the same walk
 // with the standard running max and rescale instead ([vi:Softmax], Fig. 4),
-// chosen by a branch that is uniform over the workgroup.
+// chosen by a branch that is uniform over the workgroup; that tile is a
+// separate, non-inlined function, so its registers do not crowd the bound
+// path's, and it rescales only when a row's max has grown by more than 2^8.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -59,6 +61,9 @@ typedef short v8s __attribute__((__vector_size__(8 * sizeof(short))));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Online fallback: how far (log2 units) a row's running max may lag behind the
+// true one before the accumulators are rescaled; weights stay below 2^8.
+constexpr float kRescaleSlack = 8.0f;
 
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
@@ -628,14 +633,20 @@ struct AttnKernel {
             for (int i = 1; i < NV; ++i) cm = fmaxf(cm, t[i]);
             const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(cm), __float_as_uint(cm), false, false);
             cm = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
-            const float mn = fmaxf(rw.mrow, cm);
-            const float alpha = __builtin_amdgcn_exp2f(rw.mrow - mn);
-            rw.mrow = mn;
-            rw.lsum *= alpha;
+            // rescale only when some row's max has grown by more than
+            // kRescaleSlack: until then the stale max keeps every weight below
+            // 2^kRescaleSlack, and the common shift cancels in o = O / l (the
+            // branch is uniform over the wavefront)
+            if (__any(cm > rw.mrow + kRescaleSlack)) {
+                const float mn = fmaxf(rw.mrow, cm);
+                const float alpha = __builtin_amdgcn_exp2f(rw.mrow - mn);
+                rw.mrow = mn;
+                rw.lsum *= alpha;
 #pragma unroll
-            for (int dt = 0; dt < G::DT; ++dt) rw.acc[dt] *= alpha;
+                for (int dt = 0; dt < G::DT; ++dt) rw.acc[dt] *= alpha;
+            }
 #pragma unroll
-            for (int i = 0; i < NV; ++i) pr[i] = __builtin_amdgcn_exp2f(t[i] - mn);
+            for (int i = 0; i < NV; ++i) pr[i] = __builtin_amdgcn_exp2f(t[i] - rw.mrow);
         }
 #pragma unroll
         for (int ks = 0; ks < PVK; ++ks)
@@ -832,6 +843,37 @@ struct AttnKernel {
         }
     }
 
+    // The online-fallback tile as a function of its own (not inlined): its
+    // register allocation then does not weigh on the bound path's. Its
+    // arguments arrive in vector registers; the wave-uniform ones are moved
+    // back to scalar registers so that the walk keeps its scalar cursor.
+    static __device__ __forceinline__ int32_t uni(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+    static __device__ __forceinline__ int64_t uni64(int64_t x) {
+        const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int32_t(uint64_t(x) & 0xffffffffu)));
+        const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int32_t(uint64_t(x) >> 32)));
+        return int64_t((uint64_t(hi) << 32) | lo);
+    }
+    template <typename T>
+    static __device__ __forceinline__ T *uniptr(T *x) { return reinterpret_cast<T *>(uni64(int64_t(x))); }
+
+    template <int NG>
+    static __device__ __attribute__((noinline)) void tile_online(const uint16_t *q, uint16_t *o, const int32_t *col_idx,
+                                                                 float c, int32_t seq_len, int32_t block_k,
+                                                                 int64_t head_row0, int32_t row0, int32_t nvalid,
+                                                                 const uint16_t *kh, const uint16_t *vh, int32_t e0,
+                                                                 int32_t e1, int32_t nquart) {
+        extern __shared__ __attribute__((aligned(16))) char smem[];
+        AttnParams lp = {};
+        lp.q = uniptr(q);
+        lp.o = uniptr(o);
+        lp.col_idx = uniptr(col_idx);
+        lp.c = __uint_as_float(uint32_t(uni(int32_t(__float_as_uint(c)))));
+        lp.seq_len = uni(seq_len);
+        lp.block_k = uni(block_k);
+        tile<NG, false>(lp, smem, uni64(head_row0), uni(row0), uni(nvalid), uniptr(kh), uniptr(vh), uni(e0),
+                        uni(e1), uni(nquart), true, 0.0f, nullptr);
+    }
+
     template <bool CENTRED>
     static __device__ void run(const AttnParams &p) {
         extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -874,10 +916,18 @@ struct AttnKernel {
             const int my = t0 + wave;
             const int32_t row0 = qb * p.block_q + 32 * my;
             const int nvalid = p.block_q - 32 * my < 32 ? p.block_q - 32 * my : 32;
-            if (my < ntiles)
-                tile<1, CENTRED>(p, smem, head_row0, row0, nvalid, kh, vh, e0, e1, nquart, online, mk, mu);
-            else
-                tile<0, CENTRED>(p, smem, head_row0, row0, nvalid, kh, vh, e0, e1, nquart, online, mk, mu);
+            if (online) {
+                if (my < ntiles)
+                    tile_online<1>(p.q, p.o, p.col_idx, p.c, p.seq_len, p.block_k, head_row0, row0, nvalid, kh, vh,
+                                   e0, e1, nquart);
+                else
+                    tile_online<0>(p.q, p.o, p.col_idx, p.c, p.seq_len, p.block_k, head_row0, row0, nvalid, kh, vh,
+                                   e0, e1, nquart);
+            } else if (my < ntiles) {
+                tile<1, CENTRED>(p, smem, head_row0, row0, nvalid, kh, vh, e0, e1, nquart, false, mk, mu);
+            } else {
+                tile<0, CENTRED>(p, smem, head_row0, row0, nvalid, kh, vh, e0, e1, nquart, false, mk, mu);
+            }
             if (t0 + NW < ntiles) lds_barrier();     // LDS reused by the next pass
         }
     }
