@@ -315,7 +315,8 @@ struct PreAttn {
                 const uint32_t wraps = pf / uint32_t(p.seq_len);
                 const int64_t tok = ((b0 + wraps) * p.heads * int64_t(p.seq_len) + (pf - wraps * uint32_t(p.seq_len))) * D;
                 const u32x4 v = *reinterpret_cast<const u32x4 *>(park + rw * OUT_ROW + (D * part_i + 8 * (lane % LPR)) * 2);
-                *reinterpret_cast<u32x4 *>(out + tok + 8 * (lane % LPR)) = v;
+                // streaming store: the outputs are not read again by this kernel
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(out + tok + 8 * (lane % LPR)));
             }
         }
     }
