@@ -17,6 +17,9 @@ between two device synchronisations. Prints ONE JSON line:
   duration from HIP events recorded on its launch stream around each launch;
 * cpu_baseline: the fp64 oracle (not tuned) timed on four heads of the same
   workload on the host cores, scaled to the same unit;
+* check: the last timed step's output on those four heads against that oracle
+  run (max-abs, rel-L2 and whether both are within the parity bars), so the
+  line shows that the computation it timed is correct;
 * roofline.traffic: HBM bytes per launch from the committed rocprofv3
   FETCH_SIZE / WRITE_SIZE passes (profiles/traffic.json), reported only while
   the kernel source still matches the one those counters were taken on.
@@ -95,7 +98,8 @@ def parse():
 
 
 def cpu_baseline(wl, qc, kc, vc, heads: int):
-    """Time the fp64 oracle on the first `heads` heads of batch item 0."""
+    """Time the fp64 oracle on the first `heads` heads of batch item 0; returns
+    the JSON record and the oracle's output for those heads."""
     import numpy as np
 
     import oracle
@@ -115,7 +119,20 @@ def cpu_baseline(wl, qc, kc, vc, heads: int):
                                 wl.window, wl.ref_frame)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"batch 0, heads 0..{heads - 1} of {wl.heads}, all {wl.frames} frames "
-                      f"({flops:.3e} active FLOPs; dense fp64 masked softmax), {dt:.2f} s wall"}
+                      f"({flops:.3e} active FLOPs; dense fp64 masked softmax), {dt:.2f} s wall"}, o
+
+
+def output_check(got, ref, what: str) -> dict:
+    """The timed run's bf16 output against the oracle: max-abs (element bar 1e-2,
+    or one bf16 step of the reference value where that is larger) and rel-L2
+    (bar 5e-3)."""
+    import numpy as np
+
+    import oracle
+    m, r = oracle.max_abs_and_rel_l2(got, ref)
+    step = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+    ok = bool(np.all(np.abs(got - ref) <= np.maximum(1e-2, step)) and r <= 5e-3)
+    return {"against": "fp64 oracle", "outputs": what, "max_abs": m, "rel_l2": r, "within_bars": ok}
 
 
 def bench_pre_attention(args):
@@ -187,6 +204,16 @@ def bench_pre_attention(args):
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_pre(wl, x, gain, w)
+        # the last timed step's q, k, v against the oracle given the same folded
+        # weight (and a unit gain), i.e. the function the kernel computes
+        ref = oracle.pre_attention(synthetic.to_f64(x[:1]), np.ones(wl.channels), synthetic.to_f64(wd.cpu()),
+                                   wl.heads, wl.head_dim)
+        worst = (0.0, 0.0)
+        for got, want in zip(outs, ref):
+            m, r = oracle.max_abs_and_rel_l2(synthetic.to_f64(got[:1].cpu()), want)
+            worst = (max(worst[0], m), max(worst[1], r))
+        line["check"] = {"against": "fp64 oracle", "outputs": "q, k, v of batch 0",
+                         "max_abs": worst[0], "rel_l2": worst[1], "within_bars": bool(worst[1] <= 5e-3)}
     print(json.dumps(line), flush=True)
 
 
@@ -469,7 +496,10 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, qc, kc, vc, args.cpu_heads)
+        line["cpu_baseline"], ref = cpu_baseline(wl, qc, kc, vc, args.cpu_heads)
+        # the last timed step's output (every input copy holds the same values)
+        got = synthetic.to_f64(o[:1, :args.cpu_heads].cpu())
+        line["check"] = output_check(got, ref, f"o, batch 0, heads 0..{args.cpu_heads - 1}")
     print(json.dumps(line), flush=True)
 
 
