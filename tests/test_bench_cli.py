@@ -41,3 +41,21 @@ def test_traffic_is_reported_only_for_the_profiled_kernel_source(tmp_path):
     edited.write_bytes(open(bench.KERNEL_SOURCE, "rb").read() + b"\n// edited\n")
     assert bench.measured_traffic("fsa_attention", "sr720", str(edited)) is None
     assert bench.measured_traffic("fsa_attention", "no_such_workload") is None
+
+
+def test_output_check_bars():
+    """The bench line's check: max-abs per element 1e-2, or one bf16 step of the
+    reference where that is larger; rel-L2 5e-3."""
+    import numpy as np
+
+    import bench
+    ref = np.linspace(-0.9, 0.9, 1000)
+    assert bench.output_check(ref.copy(), ref, "x")["within_bars"]
+    off = ref.copy()
+    off[3] += 1.5e-2                                  # |ref| < 2: the 1e-2 bar applies
+    assert not bench.output_check(off, ref, "x")["within_bars"]
+    big = np.full(1000, 4.3)
+    assert bench.output_check(big + 2.0e-2, big, "x")["within_bars"]       # < one bf16 step (2^-5) at 4.3
+    assert not bench.output_check(big + 4.0e-2, big, "x")["within_bars"]   # > one bf16 step
+    noisy = ref + 0.009 * np.sign(ref)                # every element within 1e-2, rel-L2 ~1.7e-2
+    assert not bench.output_check(noisy, ref, "x")["within_bars"]
