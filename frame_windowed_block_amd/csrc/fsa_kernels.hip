@@ -55,7 +55,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Read-only device data addressed uniformly: loads through the constant address
 // space are selected as scalar (SMEM) loads.
-typedef __attribute__((address_space(4))) const int32_t cint32;
+typedef __attribute__((address_space(1))) const int32_t gint32;
 typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
 typedef short v8s __attribute__((__vector_size__(8 * sizeof(short))));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
@@ -447,34 +447,42 @@ struct AttnKernel {
         u32x4 k[KL], v[KL];
     };
 
-    // The four 16-key tiles of a stage: list entries (block indices, loaded
-    // by scalar loads) and tile positions inside their blocks. The byte
-    // offsets are formed only when the stage is loaded, one stage later, so
-    // the scalar loads are in flight meanwhile. Tiles past the row end repeat
-    // the row's last tile: they are loaded but never weighted.
+    // Byte offsets (inside a head's K/V slab) of the four 16-key tiles of a stage.
     struct Src {
-        int32_t c0, c1, c2, c3;
-        int32_t j0, j1, j2, j3;
+        int32_t o0, o1, o2, o3;
     };
-    // Cursor over the row's 16-key tiles: list position e and tile j in its block.
-    struct Cursor {
-        int32_t e, j;
+    // The row's 16-key tiles as a table in one vector register: lane l of
+    // `cur` holds the byte offset of tile 64 m + l of the row's key list, so
+    // a stage takes its four offsets with v_readlane (stage s: lanes
+    // 4 (s % 16) .. + 3). The next 64 tiles' block columns (one vector load,
+    // lane l: list entry e0 + t / hpb) and tile-in-block positions are
+    // fetched when a table is taken into use, 16 stages before they are
+    // needed. Tiles past the row end repeat the row's last tile: they are
+    // loaded but never weighted. (Walking the list with a scalar cursor and
+    // scalar loads cost about 60 scalar instructions per stage and a wait on
+    // the scalar loads that also held the stage's LDS stores.)
+    struct TileTab {
+        int32_t cur, c, j;
     };
-
-    static __device__ __forceinline__ Src next_src(const cint32 *col, Cursor &cur, int32_t e1, int hpb) {
-        auto one = [&](int32_t &c, int32_t &j) {
-            c = col[cur.e < e1 ? cur.e : e1 - 1];
-            j = cur.j;
-            const bool wrap = cur.j + 1 == hpb;
-            cur.e += wrap ? 1 : 0;
-            cur.j = wrap ? 0 : cur.j + 1;
-        };
-        Src s;
-        one(s.c0, s.j0);
-        one(s.c1, s.j1);
-        one(s.c2, s.j2);
-        one(s.c3, s.j3);
-        return s;
+    static __device__ __forceinline__ void tab_fetch(const gint32 *col, int32_t e0, int32_t nquart, int hpb,
+                                                     int32_t m, TileTab &tt) {
+        int32_t t = 64 * m + int32_t(threadIdx.x & 63);
+        t = t < nquart ? t : nquart - 1;
+        const int32_t blk = int32_t(uint32_t(t) / uint32_t(hpb));
+        tt.j = t - blk * hpb;
+        tt.c = col[e0 + blk];
+    }
+    // Offsets of stage `sig` (wave-uniform, counted from 0); advances sig.
+    static __device__ __forceinline__ Src next_src(const gint32 *col, TileTab &tt, int32_t &sig, int32_t e0,
+                                                   int32_t nquart, int hpb, int bk) {
+        if ((sig & 15) == 0) {
+            tt.cur = (tt.c * bk + 16 * tt.j) * (D * 2);
+            tab_fetch(col, e0, nquart, hpb, sig / 16 + 1, tt);
+        }
+        const int i = 4 * (sig & 15);
+        ++sig;
+        return {__builtin_amdgcn_readlane(tt.cur, i), __builtin_amdgcn_readlane(tt.cur, i + 1),
+                __builtin_amdgcn_readlane(tt.cur, i + 2), __builtin_amdgcn_readlane(tt.cur, i + 3)};
     }
 
     // tile j (wave-uniform) of a stage, as a scalar select chain on values (a
@@ -515,19 +523,15 @@ struct AttnKernel {
     }
 
     static __device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
-                                                      const LoadOffsets &lo, const Src &src, int bk, Stage &st) {
+                                                      const LoadOffsets &lo, const Src &src, Stage &st) {
         const int w = wave_id();
         __builtin_assume(w >= 0 && w < NW);
-        const int32_t o0 = __builtin_amdgcn_readfirstlane((src.c0 * bk + 16 * src.j0) * (D * 2));
-        const int32_t o1 = __builtin_amdgcn_readfirstlane((src.c1 * bk + 16 * src.j1) * (D * 2));
-        const int32_t o2 = __builtin_amdgcn_readfirstlane((src.c2 * bk + 16 * src.j2) * (D * 2));
-        const int32_t o3 = __builtin_amdgcn_readfirstlane((src.c3 * bk + 16 * src.j3) * (D * 2));
 #pragma unroll
         for (int x = 0; x < KL; ++x) {
             st.k[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    krs, lo.k[x], pick(k_tile(w, x), o0, o1, o2, o3), 0));
+                                                    krs, lo.k[x], pick(k_tile(w, x), src.o0, src.o1, src.o2, src.o3), 0));
             st.v[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    vrs, lo.v[x], pick(v_row(w, x) / 16, o0, o1, o2, o3), 0));
+                                                    vrs, lo.v[x], pick(v_row(w, x) / 16, src.o0, src.o1, src.o2, src.o3), 0));
         }
     }
 
@@ -695,27 +699,28 @@ struct AttnKernel {
     // and meets every barrier.
     template <int NG, bool ONLINE>
     static __device__ __forceinline__ void walk(const AttnParams &p, char *smem, const uint16_t *kh,
-                                                const uint16_t *vh, int32_t e0, int32_t e1, int32_t nquart,
-                                                Rows &rw) {
+                                                const uint16_t *vh, int32_t e0, int32_t nquart, Rows &rw) {
         const int nst = (nquart + 3) / 4;
         if (nst == 0) return;                       // (a plan row always lists its own frame)
         const int hpb = p.block_k / 16;
-        const cint32 *col = (const cint32 *)(p.col_idx);
+        const gint32 *col = (const gint32 *)(p.col_idx);
         const int64_t slab = int64_t(p.seq_len) * D * 2;
         const __amdgpu_buffer_rsrc_t krs = head_rsrc(kh, slab), vrs = head_rsrc(vh, slab);
         const LoadOffsets lo = load_offsets();
         const StoreOffsets so = store_offsets();
         const ReadOffsets ro = read_offsets();
-        Cursor cur{e0, 0};
+        TileTab tt;
+        tab_fetch(col, e0, nquart, hpb, 0, tt);
+        int32_t sig = 0;
         Stage st;
         char *const b0 = smem, *const b1 = smem + G::STAGE, *const b2 = smem + 2 * G::STAGE;
 
-        load_stage(krs, vrs, lo, next_src(col, cur, e1, hpb), p.block_k, st);
+        load_stage(krs, vrs, lo, next_src(col, tt, sig, e0, nquart, hpb, p.block_k), st);
         store_stage(b0, so, st);
-        load_stage(krs, vrs, lo, next_src(col, cur, e1, hpb), p.block_k, st);
+        load_stage(krs, vrs, lo, next_src(col, tt, sig, e0, nquart, hpb, p.block_k), st);
         store_stage(b1, so, st);
-        load_stage(krs, vrs, lo, next_src(col, cur, e1, hpb), p.block_k, st);
-        Src nxt = next_src(col, cur, e1, hpb);
+        load_stage(krs, vrs, lo, next_src(col, tt, sig, e0, nquart, hpb, p.block_k), st);
+        Src nxt = next_src(col, tt, sig, e0, nquart, hpb, p.block_k);
         lds_barrier();
         if constexpr (NG > 0) {
             bf16x8 ka[G::KS];
@@ -728,8 +733,8 @@ struct AttnKernel {
         // per-lane offset plus an immediate.
         auto body = [&](char *bc, char *bn, char *bs) {
             store_stage(bs, so, st);
-            load_stage(krs, vrs, lo, nxt, p.block_k, st);
-            nxt = next_src(col, cur, e1, hpb);
+            load_stage(krs, vrs, lo, nxt, st);
+            nxt = next_src(col, tt, sig, e0, nquart, hpb, p.block_k);
             step<NG, ONLINE, false, true>(bc, bc + G::SUB_BYTES, ro, rw, p.c);
             step<NG, ONLINE, false, true>(bc + G::SUB_BYTES, bn, ro, rw, p.c);
             lds_barrier();
@@ -771,8 +776,7 @@ struct AttnKernel {
     template <int NG, bool CENTRED>
     static __device__ __forceinline__ void tile(const AttnParams &p, char *smem, int64_t head_row0, int32_t row0,
                                                 int nvalid, const uint16_t *kh, const uint16_t *vh, int32_t e0,
-                                                int32_t e1, int32_t nquart, bool online, float mk,
-                                                const float *mu) {
+                                                int32_t nquart, bool online, float mk, const float *mu) {
         const int lane = threadIdx.x & 63;
         const int n = lane & 31, h = lane >> 5;
         const int32_t row = row0 + (n < nvalid ? n : nvalid - 1);   // rows past the tile recompute a valid one
@@ -815,9 +819,9 @@ struct AttnKernel {
             }
         }
         if (online)
-            walk<NG, true>(p, smem, kh, vh, e0, e1, nquart, rw);
+            walk<NG, true>(p, smem, kh, vh, e0, nquart, rw);
         else
-            walk<NG, false>(p, smem, kh, vh, e0, e1, nquart, rw);
+            walk<NG, false>(p, smem, kh, vh, e0, nquart, rw);
         if constexpr (NG > 0) {
             // both halves of a row hold partial sums over disjoint keys
             const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(rw.lsum), __float_as_uint(rw.lsum),
@@ -846,7 +850,8 @@ struct AttnKernel {
     // The online-fallback tile as a function of its own (not inlined): its
     // register allocation then does not weigh on the bound path's. Its
     // arguments arrive in vector registers; the wave-uniform ones are moved
-    // back to scalar registers so that the walk keeps its scalar cursor.
+    // back to scalar registers so that the walk's stage offsets, LDS
+    // addresses and loop control stay scalar.
     static __device__ __forceinline__ int32_t uni(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
     static __device__ __forceinline__ int64_t uni64(int64_t x) {
         const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int32_t(uint64_t(x) & 0xffffffffu)));
@@ -861,7 +866,7 @@ struct AttnKernel {
                                                                  float c, int32_t seq_len, int32_t block_k,
                                                                  int64_t head_row0, int32_t row0, int32_t nvalid,
                                                                  const uint16_t *kh, const uint16_t *vh, int32_t e0,
-                                                                 int32_t e1, int32_t nquart) {
+                                                                 int32_t nquart) {
         extern __shared__ __attribute__((aligned(16))) char smem[];
         AttnParams lp = {};
         lp.q = uniptr(q);
@@ -871,7 +876,7 @@ struct AttnKernel {
         lp.seq_len = uni(seq_len);
         lp.block_k = uni(block_k);
         tile<NG, false>(lp, smem, uni64(head_row0), uni(row0), uni(nvalid), uniptr(kh), uniptr(vh), uni(e0),
-                        uni(e1), uni(nquart), true, 0.0f, nullptr);
+                        uni(nquart), true, 0.0f, nullptr);
     }
 
     template <bool CENTRED>
@@ -919,14 +924,14 @@ struct AttnKernel {
             if (online) {
                 if (my < ntiles)
                     tile_online<1>(p.q, p.o, p.col_idx, p.c, p.seq_len, p.block_k, head_row0, row0, nvalid, kh, vh,
-                                   e0, e1, nquart);
+                                   e0, nquart);
                 else
                     tile_online<0>(p.q, p.o, p.col_idx, p.c, p.seq_len, p.block_k, head_row0, row0, nvalid, kh, vh,
-                                   e0, e1, nquart);
+                                   e0, nquart);
             } else if (my < ntiles) {
-                tile<1, CENTRED>(p, smem, head_row0, row0, nvalid, kh, vh, e0, e1, nquart, false, mk, mu);
+                tile<1, CENTRED>(p, smem, head_row0, row0, nvalid, kh, vh, e0, nquart, false, mk, mu);
             } else {
-                tile<0, CENTRED>(p, smem, head_row0, row0, nvalid, kh, vh, e0, e1, nquart, false, mk, mu);
+                tile<0, CENTRED>(p, smem, head_row0, row0, nvalid, kh, vh, e0, nquart, false, mk, mu);
             }
             if (t0 + NW < ntiles) lds_barrier();     // LDS reused by the next pass
         }
