@@ -53,8 +53,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-// Read-only device data addressed uniformly: loads through the constant address
-// space are selected as scalar (SMEM) loads.
+// Device data in the global address space: loads through it are vector
+// (global_load) loads even inside a non-inlined function, whose pointer
+// arguments are otherwise generic (flat loads, which also count on the LDS
+// counter and so coarsen the LDS waits).
 typedef __attribute__((address_space(1))) const int32_t gint32;
 typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
 typedef short v8s __attribute__((__vector_size__(8 * sizeof(short))));
@@ -447,17 +449,13 @@ struct AttnKernel {
         u32x4 k[KL], v[KL];
     };
 
-    // Byte offsets (inside a head's K/V slab) of the four 16-key tiles of a stage.
-    struct Src {
-        int32_t o0, o1, o2, o3;
-    };
     // The row's 16-key tiles as a table in one vector register: lane l of
     // `cur` holds the byte offset of tile 64 m + l of the row's key list, so
-    // a stage takes its four offsets with v_readlane (stage s: lanes
-    // 4 (s % 16) .. + 3). The next 64 tiles' block columns (one vector load,
-    // lane l: list entry e0 + t / hpb) and tile-in-block positions are
-    // fetched when a table is taken into use, 16 stages before they are
-    // needed. Tiles past the row end repeat the row's last tile: they are
+    // a wavefront takes its stage tile's offset with one v_readlane (stage
+    // s, tile j of the stage: lane 4 (s % 16) + j). The next 64 tiles' block
+    // columns (one vector load, lane l: list entry e0 + t / hpb) and
+    // tile-in-block positions are fetched when a table is taken into use, 16
+    // stages before they are needed. Tiles past the row end repeat the row's last tile: they are
     // loaded but never weighted. (Walking the list with a scalar cursor and
     // scalar loads cost about 60 scalar instructions per stage and a wait on
     // the scalar loads that also held the stage's LDS stores.)
@@ -472,29 +470,20 @@ struct AttnKernel {
         tt.j = t - blk * hpb;
         tt.c = col[e0 + blk];
     }
-    // Offsets of stage `sig` (wave-uniform, counted from 0); advances sig.
-    static __device__ __forceinline__ Src next_src(const gint32 *col, TileTab &tt, int32_t &sig, int32_t e0,
-                                                   int32_t nquart, int hpb, int bk) {
+    static __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+    // Byte offset of this wavefront's tile (wave_tile()) in stage `sig`
+    // (wave-uniform, counted from 0); advances sig.
+    static __device__ __forceinline__ int32_t next_src(const gint32 *col, TileTab &tt, int32_t &sig, int32_t e0,
+                                                       int32_t nquart, int hpb, int bk) {
         if ((sig & 15) == 0) {
             tt.cur = (tt.c * bk + 16 * tt.j) * (D * 2);
             tab_fetch(col, e0, nquart, hpb, sig / 16 + 1, tt);
         }
-        const int i = 4 * (sig & 15);
+        const int i = 4 * (sig & 15) + wave_tile(wave_id());
         ++sig;
-        return {__builtin_amdgcn_readlane(tt.cur, i), __builtin_amdgcn_readlane(tt.cur, i + 1),
-                __builtin_amdgcn_readlane(tt.cur, i + 2), __builtin_amdgcn_readlane(tt.cur, i + 3)};
+        return __builtin_amdgcn_readlane(tt.cur, i);
     }
-
-    // tile j (wave-uniform) of a stage, as a scalar select chain on values (a
-    // select on field addresses would make the struct a dynamically indexed
-    // array in scratch memory)
-    static __device__ __forceinline__ int32_t pick(int j, int32_t o0, int32_t o1, int32_t o2, int32_t o3) {
-        const int32_t lo = j == 0 ? o0 : o1;
-        const int32_t hi = j == 2 ? o2 : o3;
-        return j < 2 ? lo : hi;
-    }
-
-    static __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
     // Stage loads. K: wave-wide instruction X = KL w + x covers 16 keys of one
     // tile and 4 segments (lane l: key l % 16, segment 4 (X % (SEGS / 4)) +
@@ -503,10 +492,19 @@ struct AttnKernel {
     // rows RPI X .. RPI X + RPI - 1 (lane l: row RPI X + l / SEGS, segment
     // l % SEGS). Each instruction stays inside one 16-key tile, so the tile
     // index follows from the wave index alone and the tile's offset is a
-    // scalar operand of the buffer load.
-    static __device__ __forceinline__ int k_tile(int w, int x) { return (KL * w + x) / (G::SEGS / 4); }
-    static __device__ __forceinline__ int k_segq(int w, int x) { return (KL * w + x) % (G::SEGS / 4); }
-    static __device__ __forceinline__ int v_row(int w, int x) { return RPI * (KL * w + x); }
+    // scalar operand of the buffer load. All of a wavefront's loads fall in
+    // one tile, wave_tile(w).
+    static constexpr int k_tile(int w, int x) { return (KL * w + x) / (G::SEGS / 4); }
+    static constexpr int k_segq(int w, int x) { return (KL * w + x) % (G::SEGS / 4); }
+    static constexpr int v_row(int w, int x) { return RPI * (KL * w + x); }
+    static constexpr int wave_tile(int w) { return w / (NW / 4); }
+    static constexpr bool one_tile_per_wave() {
+        for (int w = 0; w < NW; ++w)
+            for (int x = 0; x < KL; ++x)
+                if (k_tile(w, x) != wave_tile(w) || v_row(w, x) / 16 != wave_tile(w)) return false;
+        return true;
+    }
+    static_assert(NW % 4 == 0 && one_tile_per_wave(), "a wavefront's stage loads stay in one 16-key tile");
 
     struct LoadOffsets {
         int32_t k[KL], v[KL];      // bytes inside a 16-key tile
@@ -523,15 +521,11 @@ struct AttnKernel {
     }
 
     static __device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
-                                                      const LoadOffsets &lo, const Src &src, Stage &st) {
-        const int w = wave_id();
-        __builtin_assume(w >= 0 && w < NW);
+                                                      const LoadOffsets &lo, int32_t src, Stage &st) {
 #pragma unroll
         for (int x = 0; x < KL; ++x) {
-            st.k[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    krs, lo.k[x], pick(k_tile(w, x), src.o0, src.o1, src.o2, src.o3), 0));
-            st.v[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    vrs, lo.v[x], pick(v_row(w, x) / 16, src.o0, src.o1, src.o2, src.o3), 0));
+            st.k[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, lo.k[x], src, 0));
+            st.v[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, lo.v[x], src, 0));
         }
     }
 
@@ -628,15 +622,14 @@ struct AttnKernel {
 #pragma unroll
             for (int i = 0; i < NV; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(rw.s[i], c, -rw.brow));
         } else {
-            // online fallback: running max over the row (both halves), rescale
-            float t[16];
+            // online fallback: running max over the row (both halves), rescale.
+            // The max is taken on the raw scores and scaled once: c > 0 and
+            // rounding is monotonic, so it equals the max of the scaled scores.
+            float cm = rw.s[0];
 #pragma unroll
-            for (int i = 0; i < NV; ++i) t[i] = rw.s[i] * c;
-            float cm = t[0];
-#pragma unroll
-            for (int i = 1; i < NV; ++i) cm = fmaxf(cm, t[i]);
+            for (int i = 1; i < NV; ++i) cm = fmaxf(cm, rw.s[i]);
             const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(cm), __float_as_uint(cm), false, false);
-            cm = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
+            cm = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * c;
             // rescale only when some row's max has grown by more than
             // kRescaleSlack: until then the stale max keeps every weight below
             // 2^kRescaleSlack, and the common shift cancels in o = O / l (the
@@ -650,7 +643,7 @@ struct AttnKernel {
                 for (int dt = 0; dt < G::DT; ++dt) rw.acc[dt] *= alpha;
             }
 #pragma unroll
-            for (int i = 0; i < NV; ++i) pr[i] = __builtin_amdgcn_exp2f(t[i] - rw.mrow);
+            for (int i = 0; i < NV; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(rw.s[i], c, -rw.mrow));
         }
 #pragma unroll
         for (int ks = 0; ks < PVK; ++ks)
@@ -720,7 +713,7 @@ struct AttnKernel {
         load_stage(krs, vrs, lo, next_src(col, tt, sig, e0, nquart, hpb, p.block_k), st);
         store_stage(b1, so, st);
         load_stage(krs, vrs, lo, next_src(col, tt, sig, e0, nquart, hpb, p.block_k), st);
-        Src nxt = next_src(col, tt, sig, e0, nquart, hpb, p.block_k);
+        int32_t nxt = next_src(col, tt, sig, e0, nquart, hpb, p.block_k);
         lds_barrier();
         if constexpr (NG > 0) {
             bf16x8 ka[G::KS];
