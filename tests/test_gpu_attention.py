@@ -101,6 +101,14 @@ SMALL = [
     ("t1200_small", 1, 1, 128, 3, 1200, 1, 0, 240, 80),
     ("t144_d64_b2", 2, 2, 64, 4, 144, 1, 2, 144, 48),
     ("t32_dense", 1, 2, 128, 6, 32, 9, 0, 32, 32),
+    # rows whose 16-key tile counts sit at the edges of the walk's 64-tile
+    # offset tables: 64 and 128 tiles (frames 0 and 1), 65, 126 (D = 64,
+    # three tiles per block) and 129 (one tile per block, a 688-row query
+    # block taking three passes)
+    ("tab64_128", 1, 2, 128, 2, 1024, 0, 0, 256, 128),
+    ("tab65", 1, 1, 128, 1, 1040, 0, 0, 208, 80),
+    ("tab126_d64", 1, 2, 64, 2, 1008, 1, 0, 112, 48),
+    ("tab129_bk16", 1, 1, 128, 3, 688, 1, 0, 688, 16),
 ]
 
 
