@@ -203,11 +203,11 @@ __global__ __launch_bounds__(256) void norms_kernel(NormsParams p) {
     const int sub = lane / LPR;
     const int seg = lane % LPR;
 
-    if (blockIdx.x == 0) {              // accumulators of bound_reduce_kernel
+    if (blockIdx.x == 0) {              // outputs that bound_reduce_kernel folds into
         const int64_t nbh = int64_t(p.batch) * p.hc;
         for (int64_t x = threadIdx.x; x < nbh; x += blockDim.x) {
             const int64_t hb = (x / p.hc) * p.heads + p.h0 + x % p.hc;
-            p.eligible[hb] = 0;
+            p.eligible[hb] = 1;
             p.bmax[hb] = 0.0f;
         }
     }
@@ -308,7 +308,10 @@ __global__ __launch_bounds__(256) void norms_kernel(NormsParams p) {
 // fsa_bounds, kernel 2: per query block, scale * max ||q_i|| * max kmax over
 // its active key blocks. A workgroup covers 16 query blocks (16 lanes each)
 // and folds its maximum into the head's with one order-independent atomic
-// max; the last workgroup of a head to arrive writes the head's eligibility.
+// max. The head's eligibility starts at 1 (set by the norms kernel) and a
+// workgroup whose maximum exceeds the limit (or is NaN) clears it: the head
+// is eligible exactly when no query block's bound exceeds the limit, in any
+// arrival order, with no counter and no fence.
 // --------------------------------------------------------------------------
 struct ReduceParams {
     const float *qnorm, *kmax;
@@ -356,13 +359,7 @@ __global__ __launch_bounds__(256) void bound_reduce_kernel(ReduceParams p) {
         bound = nan_max(nan_max(red[0], red[1]), nan_max(red[2], red[3]));
         if (bound != bound) bound = __uint_as_float(0x7fc00000u);   // canonical NaN sorts above +inf
         atomicMax(reinterpret_cast<unsigned int *>(p.bmax + hb), __float_as_uint(bound));
-        __threadfence();
-        const int old = atomicAdd(p.eligible + hb, 1);
-        if (old == p.chunks - 1) {
-            __threadfence();
-            const float m = __uint_as_float(atomicOr(reinterpret_cast<unsigned int *>(p.bmax + hb), 0u));
-            p.eligible[hb] = (m <= p.limit) ? 1 : 0;
-        }
+        if (!(bound <= p.limit)) p.eligible[hb] = 0;
     }
 }
 
