@@ -208,7 +208,7 @@ def test_centred_head_range_and_grouping():
 
 
 # ----------------------------------------------------------------- seeded sweep of small shapes
-def _random_cases(n=24, seed=20261203):
+def _random_cases(n=24, seed=20261203, t_max=512, n_max=1536, f_max=6, prefix="rnd"):
     """Seeded random small shapes: T a multiple of 16 up to 512, block sizes
     drawn from the multiples of 16 dividing T, 1-6 frames, window 0-3, any
     reference frame, D 64 or 128, 1-2 batch items, 1-3 heads, normal or
@@ -219,12 +219,12 @@ def _random_cases(n=24, seed=20261203):
     rng = np.random.default_rng(seed)
     cases = []
     while len(cases) < n:
-        t = 16 * int(rng.integers(1, 33))
-        frames = int(rng.integers(1, 7))
-        if frames * t > 1536:
+        t = 16 * int(rng.integers(1, t_max // 16 + 1))
+        frames = int(rng.integers(1, f_max + 1))
+        if frames * t > n_max:
             continue
         divs = [16 * m for m in range(1, t // 16 + 1) if t % (16 * m) == 0]
-        cases.append((f"rnd{len(cases)}", int(rng.integers(1, 3)), int(rng.integers(1, 4)),
+        cases.append((f"{prefix}{len(cases)}", int(rng.integers(1, 3)), int(rng.integers(1, 4)),
                       int(rng.choice([64, 128])), frames, t, int(rng.integers(0, 4)),
                       int(rng.integers(0, frames)), int(rng.choice(divs)), int(rng.choice(divs)),
                       str(rng.choice(["normal", "normal", "bound_stress"]))))
@@ -232,6 +232,9 @@ def _random_cases(n=24, seed=20261203):
 
 
 RANDOM = _random_cases()
+# longer rows (N up to 4096: up to 256 16-key tiles per row), so the walk's
+# 64-tile offset tables are refilled several times at many different offsets
+WIDE = _random_cases(16, 20261205, t_max=2048, n_max=4096, f_max=8, prefix="wide")
 
 
 @pytest.mark.parametrize("case", RANDOM, ids=[c[0] for c in RANDOM])
@@ -249,6 +252,22 @@ def test_random_small_parity(case):
         o2, b2, _ = _run(wl, q, k, v, bq, bk, bound_limit=1e-30)
         assert int(b2[2].sum()) == 0
         _assert_close(synthetic.to_f64(o2), ref, name + " (online)")
+
+
+@pytest.mark.parametrize("case", WIDE, ids=[c[0] for c in WIDE])
+def test_random_wide_parity(case):
+    name, bsz, heads, d, frames, t, w, r, bq, bk, dist = case
+    wl = synthetic.Workload(name, bsz, heads, d, frames, t, w, r, dist=dist, seed=2000 + int(name[4:]) + t)
+    _say(f"case {name}: B={bsz} H={heads} D={d} F={frames} T={t} w={w} r={r} bq={bq} bk={bk} {dist}")
+    qc, kc, vc = synthetic.make_inputs(wl)
+    q, k, v = (x.cuda() for x in (qc, kc, vc))
+    ref = oracle.attention(*(synthetic.to_f64(x) for x in (qc, kc, vc)), *_oracle_args(wl))
+    o, b, dplan = _run(wl, q, k, v, bq, bk)
+    _check_bounds(wl, qc, kc, b, dplan, bq, bk)
+    _assert_close(synthetic.to_f64(o), ref, name)
+    o2, b2, _ = _run(wl, q, k, v, bq, bk, bound_limit=1e-30)
+    assert int(b2[2].sum()) == 0
+    _assert_close(synthetic.to_f64(o2), ref, name + " (online)")
 
 
 # ----------------------------------------------------------------- full-size workloads
