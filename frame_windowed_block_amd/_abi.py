@@ -141,6 +141,28 @@ def _check_qkv(name, t, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def _check_buf(name, t, dtype, shape, device):
+    """A caller-supplied device buffer must be contiguous, of the dtype and
+    shape the library indexes it with, and on the tensors' device: the C ABI
+    takes plain pointers and cannot tell an undersized buffer."""
+    if (t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous()
+            or t.device != device):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on "
+                         f"{device}; got {t.dtype} {tuple(t.shape)} on {t.device}"
+                         f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+
+
+def _check_plan(dplan, q):
+    """The plan must describe q's sequence, and its CSR must sit on q's device."""
+    torch = _torch()
+    info = dplan.info
+    n = q.shape[2]
+    if n != info.seq_len:
+        raise ValueError(f"q has {n} tokens per head but the plan covers {info.seq_len}")
+    _check_buf("plan row_ptr", dplan.row_ptr, torch.int32, (info.n_qblocks + 1,), q.device)
+    _check_buf("plan col_idx", dplan.col_idx, torch.int32, (info.nnz,), q.device)
+
+
 class DevicePlan:
     """A plan plus device copies of its CSR arrays (allocated by torch)."""
 
@@ -163,9 +185,12 @@ def bounds(dplan: DevicePlan, q, k, scale: float, bound_limit: float = 0.0,
     torch = _torch()
     _check_qkv("q", q)
     _check_qkv("k", k, q.shape)
+    _check_plan(dplan, q)
     bsz, heads, n, d = q.shape
     info = dplan.info
     dev = q.device
+    if k.device != dev:
+        raise ValueError(f"k is on {k.device}, q on {dev}")
     if qnorm is None:
         qnorm = torch.empty((bsz, heads, n), dtype=torch.float32, device=dev)
     if kmax is None:
@@ -176,6 +201,12 @@ def bounds(dplan: DevicePlan, q, k, scale: float, bound_limit: float = 0.0,
         bmax = torch.empty((bsz, heads), dtype=torch.float32, device=dev)
     if center and kmean is None:
         kmean = torch.empty((bsz, heads, d), dtype=torch.float32, device=dev)
+    _check_buf("qnorm", qnorm, torch.float32, (bsz, heads, n), dev)
+    _check_buf("kmax", kmax, torch.float32, (bsz, heads, info.n_kblocks), dev)
+    _check_buf("eligible", eligible, torch.int32, (bsz, heads), dev)
+    _check_buf("bmax", bmax, torch.float32, (bsz, heads), dev)
+    if kmean is not None:
+        _check_buf("kmean", kmean, torch.float32, (bsz, heads, d), dev)
     _check(lib().fsa_bounds(ctypes.byref(info), _ptr(dplan.row_ptr), _ptr(dplan.col_idx),
                             _ptr(q), _ptr(k), bsz, heads, d, head_offset, head_count,
                             float(scale), float(bound_limit), _ptr(qnorm), _ptr(kmax),
@@ -191,12 +222,24 @@ def attention(dplan: DevicePlan, q, k, v, qnorm, kmax, eligible, scale: float,
     _check_qkv("q", q)
     _check_qkv("k", k, q.shape)
     _check_qkv("v", v, q.shape)
+    _check_plan(dplan, q)
     bsz, heads, n, d = q.shape
+    info = dplan.info
+    dev = q.device
+    for name, t in (("k", k), ("v", v)):
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, q on {dev}")
+    _check_buf("qnorm", qnorm, torch.float32, (bsz, heads, n), dev)
+    _check_buf("kmax", kmax, torch.float32, (bsz, heads, info.n_kblocks), dev)
+    _check_buf("eligible", eligible, torch.int32, (bsz, heads), dev)
+    if kmean is not None:
+        _check_buf("kmean", kmean, torch.float32, (bsz, heads, d), dev)
     if out is None:
         out = torch.empty_like(q)
     else:
         _check_qkv("out", out, q.shape)
-    info = dplan.info
+        if out.device != dev:
+            raise ValueError(f"out is on {out.device}, q on {dev}")
     _check(lib().fsa_attention(ctypes.byref(info), _ptr(dplan.row_ptr), _ptr(dplan.col_idx),
                                _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(qnorm), _ptr(kmax),
                                _ptr(eligible), _ptr(kmean), bsz, heads, d, float(scale), head_offset,
@@ -226,12 +269,16 @@ def pre_attention(x, w_qkv, heads: int, head_dim: int, eps: float = 1e-6,
     if (w_qkv.dtype != torch.bfloat16 or tuple(w_qkv.shape) != (3 * heads * head_dim, c)
             or not w_qkv.is_contiguous()):
         raise ValueError("w_qkv must be a contiguous bf16 tensor [3 H D, C]")
+    if w_qkv.device != x.device:
+        raise ValueError(f"w_qkv is on {w_qkv.device}, x on {x.device}")
     outs = []
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t is None:
             t = torch.empty((bsz, heads, n, head_dim), dtype=torch.bfloat16, device=x.device)
         else:
             _check_qkv(name, t, (bsz, heads, n, head_dim))
+            if t.device != x.device:
+                raise ValueError(f"{name} is on {t.device}, x on {x.device}")
         outs.append(t)
     _check(lib().fsa_pre_attention(_ptr(x), _ptr(w_qkv), bsz, n, c, heads, head_dim,
                                    float(eps), float(rope_base), _ptr(outs[0]), _ptr(outs[1]),

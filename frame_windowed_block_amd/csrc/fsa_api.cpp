@@ -4,6 +4,7 @@
 // nothing and leaves every output untouched.
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 
 #include "fsa_internal.h"
 

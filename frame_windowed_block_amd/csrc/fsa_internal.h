@@ -1,6 +1,7 @@
 // Internal interface between the host-side C ABI (fsa_plan.cpp, fsa_api.cpp)
 // and the HIP kernels (fsa_kernels.hip). Plain C++: no HIP or torch types, so
-// the host logic also builds with g++ alone (for sanitizer runs on the CPU).
+// the host logic also builds with g++ alone; tests/test_host_sanitizers.py
+// builds it that way under AddressSanitizer and UndefinedBehaviorSanitizer.
 #pragma once
 
 #include <cstdint>

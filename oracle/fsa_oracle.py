@@ -56,6 +56,12 @@ the plan's closed-form block count and a hand-derived plan under
 centring: keys built as an offset plus +/- pairs of known length (so the mean
 and the centred norms are known by construction), translation invariance of
 the centred bound, and the shift bounding every active score.
+``attention_visible`` (the same definition over the visible keys only, for
+whole full-size outputs) and the second moments both attention forms return
+are pinned by the same brute force and by the constant-v closed form;
+``element_bar`` (the per-element comparison bar) by an emulation of bf16
+weights with fp32 accumulation that must stay inside it, and by outputs one
+bf16 rounding step off that must fall outside it.
 """
 from __future__ import annotations
 
@@ -113,13 +119,16 @@ def _f64(x) -> np.ndarray:
 
 
 def attention(q, k, v, frames: int, tokens_per_frame: int, window: int,
-              ref_frame: int, scale: float) -> np.ndarray:
+              ref_frame: int, scale: float, moments: bool = False):
     """o[b,h,i] = sum_j p_ij v_j / sum_j p_ij with p_ij = exp(s_ij - m_i) on the
     mask and 0 off it, s_ij = scale * q_i . k_j, m_i = max of s_ij over the mask.
 
     q, k, v: [B, H, N, D] (any float dtype, promoted to fp64). Computed dense,
     one query frame at a time: a T x N score block over every key, masked.
-    Returns fp64 [B, H, N, D], not rounded.
+    Returns fp64 [B, H, N, D], not rounded. With ``moments`` it returns
+    (o, m2), m2[b,h,i,d] = sum_j w_ij v_jd^2 with the same weights
+    w_ij = p_ij / sum_j p_ij (the second moment of v under row i's attention,
+    used by ``element_bar``).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     bsz, heads, n, _ = q.shape
@@ -128,6 +137,7 @@ def attention(q, k, v, frames: int, tokens_per_frame: int, window: int,
     vis = frame_visibility(frames, window, ref_frame)
     key_frame = np.arange(n) // t
     out = np.empty_like(q)
+    m2 = np.empty_like(v) if moments else None
     for b in range(bsz):
         for h in range(heads):
             kt = k[b, h].T
@@ -138,8 +148,43 @@ def attention(q, k, v, frames: int, tokens_per_frame: int, window: int,
                 s = np.where(on[None, :], s, -np.inf)
                 m = s.max(axis=1, keepdims=True)
                 p = np.exp(s - m)                                 # exactly 0 off the mask
-                out[b, h, rows] = (p @ v[b, h]) / p.sum(axis=1, keepdims=True)
-    return out
+                z = p.sum(axis=1, keepdims=True)
+                out[b, h, rows] = (p @ v[b, h]) / z
+                if moments:
+                    m2[b, h, rows] = (p @ (v[b, h] * v[b, h])) / z
+    return (out, m2) if moments else out
+
+
+def attention_visible(q, k, v, frames: int, tokens_per_frame: int, window: int,
+                      ref_frame: int, scale: float, moments: bool = False):
+    """The same masked softmax attention as ``attention``, with each query
+    frame's scores formed only against the keys of its visible frames V(f)
+    (the window plus the reference frame, [vi:Mask]). Off-mask weights are
+    exactly zero in the definition, so leaving those keys out changes nothing
+    but the order in which fp64 sums meet their exact zeros. It needs a
+    fraction (the mask density) of the dense form's work, which makes whole
+    full-size outputs affordable to check. Returns what ``attention`` does.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    bsz, heads, n, _ = q.shape
+    t = tokens_per_frame
+    assert n == frames * t
+    out = np.empty_like(q)
+    m2 = np.empty_like(v) if moments else None
+    for f in range(frames):
+        rows = slice(f * t, (f + 1) * t)
+        keys = np.concatenate([np.arange(g * t, (g + 1) * t)
+                               for g in visible_frames(f, frames, window, ref_frame)])
+        for b in range(bsz):
+            for h in range(heads):
+                kk, vv = k[b, h, keys], v[b, h, keys]
+                s = scale * (q[b, h, rows] @ kk.T)                # [T, |V(f)| T]
+                p = np.exp(s - s.max(axis=1, keepdims=True))
+                z = p.sum(axis=1, keepdims=True)
+                out[b, h, rows] = (p @ vv) / z
+                if moments:
+                    m2[b, h, rows] = (p @ (vv * vv)) / z
+    return (out, m2) if moments else out
 
 
 def attention_rows(q, k, v, rows, frames: int, tokens_per_frame: int, window: int,
@@ -165,7 +210,7 @@ def attention_rows(q, k, v, rows, frames: int, tokens_per_frame: int, window: in
             s = scale * (kk @ _f64(q[b, h, i]))                   # [N]
             on = vis[i // t][key_frame]
             shift = s[on].max() if row_bound is None else float(row_bound[b, h, i])
-            p = np.where(on, np.exp(s - shift), 0.0)
+            p = np.exp(np.where(on, s - shift, -np.inf))         # exactly 0 off the mask
             out[r] = (p @ vv) / p.sum()
     return out
 
@@ -451,6 +496,56 @@ def active_flops(batch: int, heads: int, head_dim: int, frames: int, tokens_per_
     return 4 * head_dim * batch * heads * active_pairs(frames, tokens_per_frame, window, ref_frame)
 
 
+MAX_ABS_BAR = 1e-2
+REL_L2_BAR = 5e-3
+
+
+def bf16_ulp(x) -> np.ndarray:
+    """Spacing of bf16 numbers (8 significant bits) at |x| (normal range)."""
+    e = np.floor(np.log2(np.maximum(np.abs(_f64(x)), 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def _gamma(n) -> np.ndarray:
+    """Classic bound n u / (1 - n u) on the relative error of n fp32 roundings."""
+    nu = _f64(n) * 2.0 ** -24
+    return nu / (1.0 - nu)
+
+
+def element_bar(ref, m2, score_bound, n_keys, head_dim: int) -> np.ndarray:
+    """Per-element max-abs bar for a bf16 output against the fp64 result ``ref``.
+
+    The target bar is 1e-2. An element may exceed it only where correct bf16 /
+    fp32 arithmetic itself can: the bar is max(1e-2, ulp(|ref| + e) / 2 + e),
+    with e the worst-case error of the fp32 value before the final rounding
+    to bf16 (half a bf16 spacing):
+
+    * weights rounded to bf16 (relative 2^-8 each) and perturbed by the fp32
+      score error (at most gamma_D * scale ||q_i|| ||k_j|| <= gamma_D * B_i with
+      B_i = ``score_bound``, the row's Cauchy-Schwarz bound over its visible
+      keys, plus 2^-20 (1 + B_i) for the exponent's own roundings): each
+      weight p_j becomes p_j (1 + eps_j), |eps_j| <= rho = (1 + 2^-8) exp(eta) - 1.
+      The row sum adds the same weights, so the result is
+      o + sum_j p_j eps_j (v_j - o) / sum_j p_j (1 + eps_j) (the terms
+      p_j (v_j - o) alone sum to zero); with 1 + eps_j >= (1 - 2^-8) exp(-eta)
+      that is at most rho exp(eta) / (1 - 2^-8) times
+      sum_j w_j |v_j - o| <= sigma = sqrt(m2 - o^2) (Jensen) away from o;
+    * fp32 accumulation of the weighted values in 16-key products (depth
+      n/16 + 16 for n = ``n_keys``) and of the row sum per lane in pairs
+      (depth n/4 + 4): (gamma_{n/16+16} + gamma_{n/4+4}) sqrt(m2).
+
+    ref, m2: [..., D]; score_bound, n_keys: [...] (broadcast over D)."""
+    ref, m2 = _f64(ref), _f64(m2)
+    b = _f64(score_bound)[..., None]
+    n = _f64(n_keys)[..., None]
+    eta = _gamma(head_dim) * b + 2.0 ** -20 * (1.0 + b)
+    rho = (1.0 + 2.0 ** -8) * np.exp(eta) - 1.0
+    sigma = np.sqrt(np.maximum(m2 - ref * ref, 0.0))
+    e = rho * np.exp(eta) / (1.0 - 2.0 ** -8) * sigma
+    e = e + (_gamma(n / 16.0 + 16.0) + _gamma(n / 4.0 + 4.0)) * np.sqrt(np.maximum(m2, 0.0))
+    return np.maximum(MAX_ABS_BAR, 0.5 * bf16_ulp(np.abs(ref) + e) + e)
+
+
 def max_abs_and_rel_l2(got, ref) -> tuple[float, float]:
     """The two comparison metrics: max |got - ref| and ||got - ref||_2 / ||ref||_2."""
     got, ref = _f64(got), _f64(ref)
@@ -463,10 +558,11 @@ def max_abs_and_rel_l2(got, ref) -> tuple[float, float]:
 
 __all__ = [
     "DEFAULT_BOUND_LIMIT", "visible_frames", "frame_visibility", "token_mask_rows",
-    "token_mask", "attention", "attention_rows", "attention_weights",
+    "token_mask", "attention", "attention_visible", "attention_rows", "attention_weights",
     "attention_bound_shift", "aligned_block_sizes", "auto_block_sizes", "block_classes",
     "check_plan_args", "plan", "effective_bound_limit", "bounds", "row_bound_by_frames",
-    "active_pairs", "active_flops", "max_abs_and_rel_l2",
+    "active_pairs", "active_flops", "max_abs_and_rel_l2", "MAX_ABS_BAR", "REL_L2_BAR", "bf16_ulp",
+    "element_bar",
     "DEFAULT_RMS_EPS", "DEFAULT_ROPE_BASE", "rms_norm", "rope_frequencies", "rope", "pre_attention",
     "pre_attention_flops",
 ]

@@ -43,10 +43,12 @@ def brute_visible(f, frames, window, ref_frame):
     return out
 
 
-def brute_attention(q, k, v, frames, t, window, ref_frame, scale):
-    """Masked softmax attention with Python loops and math.exp (tiny inputs)."""
+def brute_attention(q, k, v, frames, t, window, ref_frame, scale, moments=False):
+    """Masked softmax attention with Python loops and math.exp (tiny inputs);
+    with ``moments`` also the weighted mean of v squared."""
     bsz, heads, n, d = q.shape
     o = np.zeros_like(q)
+    m2 = np.zeros_like(q)
     for b in range(bsz):
         for h in range(heads):
             for i in range(n):
@@ -58,7 +60,8 @@ def brute_attention(q, k, v, frames, t, window, ref_frame, scale):
                 z = sum(w)
                 for c in range(d):
                     o[b, h, i, c] = sum(wj * v[b, h, j, c] for wj, j in zip(w, keys)) / z
-    return o
+                    m2[b, h, i, c] = sum(wj * v[b, h, j, c] ** 2 for wj, j in zip(w, keys)) / z
+    return (o, m2) if moments else o
 
 
 def check_golden_attention(orc):
@@ -101,9 +104,16 @@ def check_brute_force(orc, cases=BRUTE_CASES):
         n = frames * t
         q, k, v = (_rand((1, 2, n, d), 100 * idx + s) for s in range(3))
         scale = 1.0 / math.sqrt(d)
-        ref = brute_attention(q, k, v, frames, t, w, r, scale)
+        ref, ref_m2 = brute_attention(q, k, v, frames, t, w, r, scale, moments=True)
         got = orc.attention(q, k, v, frames, t, w, r, scale)
         np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+        # the same definition over the visible keys only, and the second moment
+        for fn in (orc.attention, orc.attention_visible):
+            got, got_m2 = fn(q, k, v, frames, t, w, r, scale, moments=True)
+            np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(got_m2, ref_m2, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(orc.attention_visible(q, k, v, frames, t, w, r, scale), ref,
+                                   rtol=0, atol=1e-12)
         rows = [(0, 1, 0), (0, 0, n - 1), (0, 1, n // 2)]
         got_rows = orc.attention_rows(q, k, v, rows, frames, t, w, r, scale)
         for x, (b, h, i) in enumerate(rows):
@@ -116,6 +126,14 @@ def check_weights(orc):
     q, k = _rand((1, 2, n, d), 7), _rand((1, 2, n, d), 8)
     p = orc.attention_weights(q, k, frames, t, w, r, 1.0 / math.sqrt(d))
     np.testing.assert_allclose(p.sum(-1), 1.0, rtol=0, atol=1e-12)
+    # each row equals the brute-force weights, exp(s - max) / sum, scale included
+    for b_h in range(2):
+        for i in (0, t - 1, n // 2, n - 1):
+            vis = brute_visible(i // t, frames, w, r)
+            keys = [j for j in range(n) if (j // t) in vis]
+            s = [sum(q[0, b_h, i, c] * k[0, b_h, j, c] for c in range(d)) / math.sqrt(d) for j in keys]
+            e = [math.exp(x - max(s)) for x in s]
+            np.testing.assert_allclose(p[0, b_h, i, keys], np.array(e) / sum(e), rtol=0, atol=1e-13)
     for i in range(n):
         vis = brute_visible(i // t, frames, w, r)
         for j in range(n):
@@ -160,6 +178,10 @@ def check_closed_forms(orc):
     const_v = np.broadcast_to(np.array([1.5, -2.0, 0.0, 3.25, 7.0]), (1, 1, n, d)).copy()
     o = orc.attention(q, k, const_v, frames, t, w, r, scale)
     np.testing.assert_allclose(o, const_v, rtol=0, atol=1e-12)
+    for fn in (orc.attention, orc.attention_visible):
+        o, m2 = fn(q, k, const_v, frames, t, w, r, scale, moments=True)
+        np.testing.assert_allclose(o, const_v, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(m2, const_v ** 2, rtol=1e-13, atol=1e-12)
     # frame-indicator v: column c = [frame(j) == c] -> attention mass per frame
     ind_v = np.zeros((1, 1, n, frames))
     for j in range(n):
@@ -482,9 +504,90 @@ def check_pre_attention(orc):
     np.testing.assert_allclose(q[0, :, 0].reshape(-1), w[:heads * d] @ xn, rtol=0, atol=1e-12)
 
 
+def _bf16(x):
+    """Round to bf16 (RNE) and back to fp32."""
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def emulate_bf16_kernel(q, k, v, frames, t, window, ref_frame, scale, shift="bound"):
+    """Masked attention in the arithmetic of a bf16 MFMA kernel, emulated with
+    numpy fp32 on bf16-valued inputs (independent of the oracle): fp32 scores,
+    weights exp2(s c - shift) with c = scale log2(e), rounded to bf16; values
+    accumulated in fp32 sixteen keys at a time, the row sum of the same bf16
+    weights in fp32 pairs; o = O / l rounded to bf16. ``shift`` is the row's
+    Cauchy-Schwarz bound times log2(e) ("bound") or the row max ("max")."""
+    f32 = np.float32
+    bsz, heads, n, d = q.shape
+    c = f32(f32(scale) * f32(math.log2(math.e)))
+    out = np.zeros(q.shape)
+    qf, kf, vf = (np.asarray(x, dtype=np.float32) for x in (q, k, v))
+    for b in range(bsz):
+        for h in range(heads):
+            kn = np.sqrt((kf[b, h].astype(np.float64) ** 2).sum(-1)).astype(np.float32)
+            for i in range(n):
+                keys = [j for j in range(n) if (j // t) in brute_visible(i // t, frames, window, ref_frame)]
+                sc = (kf[b, h, keys] @ qf[b, h, i]).astype(np.float32)
+                if shift == "bound":
+                    qn = f32(np.sqrt((qf[b, h, i].astype(np.float64) ** 2).sum()))
+                    sh = f32(c * f32(qn * kn[keys].max()))
+                else:
+                    sh = f32((sc * c).max())
+                x = (sc.astype(np.float64) * float(c) - float(sh)).astype(np.float32)
+                p = _bf16(np.exp2(x))
+                acc = np.zeros(d, dtype=np.float32)
+                lsum = f32(0.0)
+                for j0 in range(0, len(keys), 16):
+                    part = p[j0:j0 + 16].astype(np.float64) @ vf[b, h, keys[j0:j0 + 16]].astype(np.float64)
+                    acc = (acc + part.astype(np.float32)).astype(np.float32)
+                for j0 in range(0, len(keys), 2):
+                    lsum = f32(lsum + f32(p[j0:j0 + 2].sum()))
+                out[b, h, i] = _bf16(acc / lsum)
+    return out
+
+
+def check_element_bar(orc):
+    """The per-element bar admits correct bf16 / fp32 arithmetic and nothing
+    looser where it counts: an emulation of that arithmetic stays inside it on
+    plain, heavy-tailed and large-output inputs; the bar is 1e-2 on almost
+    every plain element; where |o| >= 4 it stays below one bf16 spacing, so an
+    output one rounding step off fails it."""
+    frames, t, d, w, r = 4, 32, 16, 1, 0
+    n = frames * t
+    scale = 1.0 / math.sqrt(d)
+    cases = []
+    q, k, v = (_bf16(_rand((1, 2, n, d), 500 + s)) for s in range(3))
+    cases.append(("normal", q, k, v, "bound"))
+    zq, zk = _rand((1, 2, n, 1), 510), _rand((1, 2, n, 1), 511)
+    big = np.ones((1, 2, n, 1))
+    big[:, :, ::20] = 8.0
+    cases.append(("heavy", _bf16(q * np.exp(zq)), _bf16(k * np.exp(zk) * big), v, "max"))
+    # nearly one-hot rows over values of spread 6: outputs reach |o| >= 4
+    cases.append(("large", _bf16(10.0 * q), k, _bf16(6.0 * v), "max"))
+    for name, qq, kk, vv, sh in cases:
+        ref, m2 = orc.attention(qq, kk, vv, frames, t, w, r, scale, moments=True)
+        sb = orc.row_bound_by_frames(qq, kk, frames, t, w, r, scale)
+        nk = np.array([len(brute_visible(i // t, frames, w, r)) * t for i in range(n)])
+        bar = orc.element_bar(ref, m2, sb, np.broadcast_to(nk, sb.shape), d)
+        emu = emulate_bf16_kernel(qq, kk, vv, frames, t, w, r, scale, sh)
+        assert np.all(np.abs(emu - ref) <= bar), (name, float((np.abs(emu - ref) - bar).max()))
+        if name == "normal":
+            assert np.all(bar == 1e-2), name
+        if name == "large":
+            # where |o| >= 4 and the row is nearly one-hot the bar stays under
+            # one bf16 spacing, and correct arithmetic does exceed 1e-2 there
+            hi = (np.abs(ref) >= 4.0) & (m2 - ref * ref < 0.25)
+            assert hi.sum() >= 100, name
+            assert np.all(bar[hi] < orc.bf16_ulp(ref[hi])), name
+            assert np.any(np.abs(emu - ref)[hi] > 1e-2), name
+    # a zero-spread element: the bar is 1e-2 below |o| = 2 and half a spacing above 4
+    ref = np.array([[0.3, 3.0, 5.0, -6.5]])
+    bar = orc.element_bar(ref, ref * ref, np.ones(1), np.full(1, 64), 128)
+    np.testing.assert_allclose(bar[0], [1e-2, 1e-2, 2.0 ** -6 / 2 * 2, 2.0 ** -6 / 2 * 2], rtol=1e-3)
+
+
 ALL_CHECKS = [
     check_golden_attention, check_golden_plans, check_brute_force, check_weights,
     check_dense_limit, check_closed_forms, check_bound_shift_exact, check_cauchy_schwarz,
     check_plan_closed_form, check_plan_negative_control, check_invariances, check_centering,
-    check_pre_attention,
+    check_pre_attention, check_element_bar,
 ]

@@ -25,7 +25,7 @@ def test_help_lists_the_kernels_and_options():
     r = _run("--help")
     assert r.returncode == 0
     for opt in ("--gpus", "--steps", "--warmup", "--workload", "--no-cpu-baseline", "--center",
-                "--groups", "--kernel", "--copy-calibration"):
+                "--groups", "--kernel", "--copy-calibration", "--preroll-ms"):
         assert opt in r.stdout, opt
     for kernel in ("attention", "pre_attention", "chain"):
         assert kernel in r.stdout, kernel
@@ -44,18 +44,26 @@ def test_traffic_is_reported_only_for_the_profiled_kernel_source(tmp_path):
 
 
 def test_output_check_bars():
-    """The bench line's check: max-abs per element 1e-2, or one bf16 step of the
-    reference where that is larger; rel-L2 5e-3."""
+    """The bench line's check: every element within the oracle's element bar
+    (1e-2, raised to half a bf16 spacing plus the arithmetic's error only where
+    that is larger) and rel-L2 5e-3."""
     import numpy as np
 
     import bench
-    ref = np.linspace(-0.9, 0.9, 1000)
-    assert bench.output_check(ref.copy(), ref, "x")["within_bars"]
+
+    def check(got, ref, spread=0.0):
+        m2 = ref * ref + spread ** 2
+        sb = np.full(ref.shape[:-1], 20.0)
+        nk = np.full(ref.shape[:-1], 4800)
+        return bench.output_check(got, ref, m2, sb, nk, 128, "x")["within_bars"]
+
+    ref = np.linspace(-0.9, 0.9, 1024).reshape(8, 128)
+    assert check(ref.copy(), ref)
     off = ref.copy()
-    off[3] += 1.5e-2                                  # |ref| < 2: the 1e-2 bar applies
-    assert not bench.output_check(off, ref, "x")["within_bars"]
-    big = np.full(1000, 4.3)
-    assert bench.output_check(big + 2.0e-2, big, "x")["within_bars"]       # < one bf16 step (2^-5) at 4.3
-    assert not bench.output_check(big + 4.0e-2, big, "x")["within_bars"]   # > one bf16 step
+    off[0, 3] += 1.5e-2                               # |ref| < 2: the 1e-2 bar applies
+    assert not check(off, ref)
+    big = np.full((8, 128), 4.3)
+    assert check(big + 1.5e-2, big)                   # within half a bf16 spacing (2^-6) at 4.3
+    assert not check(big + 2.0e-2, big)               # more than half a spacing: off by a rounding step
     noisy = ref + 0.009 * np.sign(ref)                # every element within 1e-2, rel-L2 ~1.7e-2
-    assert not bench.output_check(noisy, ref, "x")["within_bars"]
+    assert not check(noisy, ref)

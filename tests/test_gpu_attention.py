@@ -2,14 +2,12 @@
 
 Bars: block plans bit-exact (CPU tests), bounds within 1e-5 relative, and
 attention outputs (bf16) within relative L2 5e-3 of the oracle and, element
-by element, within max-abs 1e-2 or one bf16 step of the reference value where
-that step is larger (|o| >= 2, reached on heavy-tailed inputs whose rows are
-nearly one-hot: there rounding the exact result to bf16 alone can move it by
-more than 1e-2). Small shapes are compared element by element on every output; the
-full-size workloads on seeded samples of rows (the oracle computes those rows
-exactly) plus whole-tensor properties.
+by element, within the bar of ``oracle.element_bar``: max-abs 1e-2, raised
+only where correct bf16 / fp32 arithmetic can itself exceed it (half a bf16
+spacing of the result plus the worst-case error of bf16 weights and fp32
+accumulation, which matters only at |o| >= 4 on nearly one-hot rows). Every
+output element of every shape is compared, the full-size workloads included.
 """
-import math
 import sys
 
 import numpy as np
@@ -18,11 +16,10 @@ import torch
 
 import oracle
 import synthetic
+from tests import parity
 
 pytestmark = pytest.mark.gpu
 
-MAX_ABS = 1e-2
-REL_L2 = 5e-3
 BOUND_RTOL = 1e-5
 
 
@@ -51,20 +48,8 @@ def _oracle_args(wl):
     return (wl.frames, wl.tokens_per_frame, wl.window, wl.ref_frame, wl.scale)
 
 
-def _bf16_step(x):
-    """Spacing of bf16 numbers (8 significant bits) at |x|."""
-    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
-    return 2.0 ** (e - 7)
-
-
 def _assert_close(got, ref, what):
-    m, r = oracle.max_abs_and_rel_l2(got, ref)
-    bar = np.maximum(MAX_ABS, _bf16_step(ref))
-    excess = float((np.abs(got - ref) - bar).max()) if got.size else 0.0
-    _say(f"{what}: max_abs={m:.3e} rel_l2={r:.3e} worst excess over the bar={excess:.3e}")
-    assert np.isfinite(got).all(), what
-    assert excess <= 0.0, (what, m, excess)
-    assert r <= REL_L2, (what, r)
+    parity.assert_close(got, ref, what)
 
 
 def _check_bounds(wl, qc, kc, b, dplan, bq, bk, bound_limit=0.0, center=False):
@@ -121,7 +106,7 @@ def test_small_parity(case):
     q, k, v = (x.cuda() for x in (qc, kc, vc))
     o, b, dplan = _run(wl, q, k, v, bq, bk)
     _check_bounds(wl, qc, kc, b, dplan, bq, bk)
-    ref = oracle.attention(*(synthetic.to_f64(x) for x in (qc, kc, vc)), *_oracle_args(wl))
+    ref = parity.reference(wl, qc, kc, vc)
     _assert_close(synthetic.to_f64(o), ref, name)
     # online fallback forced on every head: same result within tolerance
     o2, b2, _ = _run(wl, q, k, v, bq, bk, bound_limit=1e-30)
@@ -151,7 +136,7 @@ def test_centred_parity(case):
     _say(f"case {name}: B={bsz} H={heads} D={d} F={frames} T={t} w={w} r={r} bq={bq} bk={bk} centred")
     qc, kc, vc = synthetic.make_inputs(wl)
     q, k, v = (x.cuda() for x in (qc, kc, vc))
-    ref = oracle.attention(*(synthetic.to_f64(x) for x in (qc, kc, vc)), *_oracle_args(wl))
+    ref = parity.reference(wl, qc, kc, vc)
     o, b, dplan = _run(wl, q, k, v, bq, bk, center=True)
     rb = _check_bounds(wl, qc, kc, b, dplan, bq, bk, center=True)
     assert np.all(rb["eligible"] == 1)
@@ -172,7 +157,7 @@ def test_centred_on_zero_mean_keys_matches_plain():
     o2, b2, _ = _run(wl, q, k, v, center=True)
     assert torch.equal(o1, o2) and torch.equal(b1[4], b2[4])
     _check_bounds(wl, qc, kc, b1, dplan, 0, 0, center=True)
-    ref = oracle.attention(*(synthetic.to_f64(x) for x in (qc, kc, vc)), *_oracle_args(wl))
+    ref = parity.reference(wl, qc, kc, vc)
     _assert_close(synthetic.to_f64(o1), ref, "centred on zero-mean keys")
 
 
@@ -246,7 +231,7 @@ def test_random_small_parity(case):
     q, k, v = (x.cuda() for x in (qc, kc, vc))
     o, b, dplan = _run(wl, q, k, v, bq, bk)
     _check_bounds(wl, qc, kc, b, dplan, bq, bk)
-    ref = oracle.attention(*(synthetic.to_f64(x) for x in (qc, kc, vc)), *_oracle_args(wl))
+    ref = parity.reference(wl, qc, kc, vc)
     _assert_close(synthetic.to_f64(o), ref, name)
     if int(name[3:]) % 3 == 0:
         o2, b2, _ = _run(wl, q, k, v, bq, bk, bound_limit=1e-30)
@@ -261,7 +246,7 @@ def test_random_wide_parity(case):
     _say(f"case {name}: B={bsz} H={heads} D={d} F={frames} T={t} w={w} r={r} bq={bq} bk={bk} {dist}")
     qc, kc, vc = synthetic.make_inputs(wl)
     q, k, v = (x.cuda() for x in (qc, kc, vc))
-    ref = oracle.attention(*(synthetic.to_f64(x) for x in (qc, kc, vc)), *_oracle_args(wl))
+    ref = parity.reference(wl, qc, kc, vc)
     o, b, dplan = _run(wl, q, k, v, bq, bk)
     _check_bounds(wl, qc, kc, b, dplan, bq, bk)
     _assert_close(synthetic.to_f64(o), ref, name)
@@ -284,14 +269,14 @@ def _full(name):
     return _cache[name]
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", FULL)
 def test_full_parity(name):
+    """Every output element of the full-size workload against the oracle."""
     wl, qc, kc, vc = _full(name)
     _say(f"workload {name}: N={wl.seq_len} H={wl.heads} D={wl.head_dim}")
     q, k, v = (x.cuda() for x in (qc, kc, vc))
-    rows = synthetic.sample_rows(wl, 256 if wl.seq_len > 1000 else 400)
-    ref = oracle.attention_rows(synthetic.to_f64(qc), synthetic.to_f64(kc), synthetic.to_f64(vc),
-                                rows, *_oracle_args(wl))
+    ref = parity.reference(wl, qc, kc, vc)
     # the key-offset workload needs centring for the bound path; run it both ways
     for center in ((False, True) if name == "key_offset" else (False,)):
         o, b, dplan = _run(wl, q, k, v, center=center)
@@ -301,10 +286,7 @@ def test_full_parity(name):
             assert np.all(eligible == 0)
         else:
             assert np.all(eligible == 1)
-        assert torch.isfinite(o).all().item()
-        oc = o.cpu()
-        got = np.stack([synthetic.to_f64(oc[bb, hh, ii]) for bb, hh, ii in rows])
-        _assert_close(got, ref, name + (" (centred)" if center else ""))
+        _assert_close(synthetic.to_f64(o), ref, name + (" (centred)" if center else ""))
 
 
 def test_deterministic_and_grouping_bitwise():
@@ -355,8 +337,7 @@ def test_head_range_leaves_other_heads_untouched():
         assert torch.all(qn[:, h] == -1.0) and torch.all(km[:, h] == -1.0)
         assert torch.all(el[:, h] == -3) and torch.all(bm[:, h] == -1.0)
     assert torch.all(el[:, 1:4] == 1)
-    ref = oracle.attention(*(synthetic.to_f64(x[:, 1:4]) for x in (qc, kc, vc)),
-                           *_oracle_args(wl))
+    ref = parity.select_heads(parity.reference(wl, qc, kc, vc), slice(1, 4))
     _assert_close(synthetic.to_f64(sentinel[:, 1:4]), ref, "head range")
 
 

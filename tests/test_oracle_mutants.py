@@ -200,6 +200,39 @@ def _plan_swapped_sizes(frames, t, window, ref_frame, block_q=0, block_k=0):
     return oracle.plan(frames, t, window, ref_frame, block_k, block_q)
 
 
+def _visible_window_only(q, k, v, frames, t, window, ref_frame, scale, moments=False):
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    out, m2 = np.empty_like(q), np.empty_like(v)
+    for f in range(frames):
+        rows = slice(f * t, (f + 1) * t)
+        keys = np.arange(max(0, f - window) * t, (min(frames - 1, f + window) + 1) * t)
+        s = scale * (q[:, :, rows] @ np.swapaxes(k[:, :, keys], -1, -2))
+        p = np.exp(s - s.max(-1, keepdims=True))
+        z = p.sum(-1, keepdims=True)
+        out[:, :, rows] = (p @ v[:, :, keys]) / z
+        m2[:, :, rows] = (p @ v[:, :, keys] ** 2) / z
+    return (out, m2) if moments else out
+
+
+def _moment_of_mean(fn):
+    def wrapped(q, k, v, frames, t, window, ref_frame, scale, moments=False):
+        if not moments:
+            return fn(q, k, v, frames, t, window, ref_frame, scale)
+        o = fn(q, k, v, frames, t, window, ref_frame, scale)
+        return o, o * o
+    return wrapped
+
+
+def _bar_no_half_spacing(ref, m2, score_bound, n_keys, head_dim):
+    return np.minimum(oracle.element_bar(ref, m2, score_bound, n_keys, head_dim),
+                      np.maximum(1e-2, oracle.element_bar(ref, m2, score_bound, n_keys, head_dim)
+                                 - 0.5 * oracle.bf16_ulp(ref)))
+
+
+def _bar_full_spacing(ref, m2, score_bound, n_keys, head_dim):
+    return np.maximum(1e-2, oracle.bf16_ulp(ref))
+
+
 MUTANTS = {
     "reference frame dropped": dict(module={"visible_frames": _vis_no_ref}),
     "window wraps around": dict(module={"visible_frames": _vis_wrap}),
@@ -229,6 +262,11 @@ MUTANTS = {
     "rms taken over tokens": dict(module={"rms_norm": _rms_over_tokens}),
     "norm gain dropped": dict(module={"rms_norm": _rms_no_gain}),
     "rms without the square root": dict(module={"rms_norm": _rms_no_sqrt}),
+    "visible-key attention without the reference frame": dict(ns={"attention_visible": _visible_window_only}),
+    "second moment taken as the squared mean": dict(ns={"attention_visible": _moment_of_mean(
+        oracle.attention_visible)}),
+    "element bar without the half bf16 spacing": dict(ns={"element_bar": _bar_no_half_spacing}),
+    "element bar widened to one bf16 spacing": dict(ns={"element_bar": _bar_full_spacing}),
     "key blocks listed descending": dict(ns={"plan": _plan_descending}),
     "query and key block sizes swapped": dict(ns={"plan": _plan_swapped_sizes}),
 }
