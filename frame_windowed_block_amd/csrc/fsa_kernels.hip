@@ -43,6 +43,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <type_traits>
 
 #include "fsa_internal.h"
 
@@ -61,6 +62,7 @@ typedef __attribute__((address_space(1))) const int32_t gint32;
 typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
 typedef short v8s __attribute__((__vector_size__(8 * sizeof(short))));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
 // Online fallback: how far (log2 units) a row's running max may lag behind the
@@ -379,21 +381,33 @@ struct AttnParams {
 };
 
 // Geometry of one LDS stage: 64 keys = two 32-key sub-steps, each holding K
-// segment-major, [D/8 segments][32 keys][8 d] (16 bytes per key and segment),
-// then V row-major with rows padded to VRS bytes.
+// as two 16-key tiles, segment-major inside a tile ([D/8 segments][16 keys]
+// [16 bytes]), then V row-major without padding, its 16-byte segments
+// permuted per row (segment s of row r sits in slot s ^ vswz(r)). Both are
+// what direct global -> LDS loads write: each load instruction fills 1 KB of
+// LDS in lane order.
 template <int D>
 struct Geo {
     static constexpr int SEGS = D / 8;             // 16-byte segments per K / V row
     static constexpr int KS = D / 16;              // q.k MFMA steps over d (16 each)
     static constexpr int DT = D / 32;              // 32-wide output column tiles
-    static constexpr int SUB_K = 32 * D * 2;
-    // V rows padded by 64 bytes: the transposing reads of four consecutive
-    // rows then fall in four different 64-byte bank groups
-    static constexpr int VRS = 2 * D + 64;
-    static constexpr int SUB_V = 32 * VRS;
+    static constexpr int ROWB = 2 * D;             // bytes per K / V row
+    static constexpr int TILE_K = 16 * ROWB;       // one 16-key K tile
+    static constexpr int SUB_K = 2 * TILE_K;
+    static constexpr int SUB_V = 32 * ROWB;
     static constexpr int SUB_BYTES = SUB_K + SUB_V;
     static constexpr int STAGE = 2 * SUB_BYTES;
+    static constexpr int RPL = 256 / ROWB;         // V rows per 256-byte line of the 64 LDS banks
 };
+
+// V segment permutation. The transposing V reads of a half wave touch rows
+// r0 .. r0 + 3 (r0 a multiple of 4) at the four segments of one 32-wide
+// column tile; XOR-ing bits 2 and 3 of the segment index with the row's
+// position (in 256-byte lines) spreads those 16 segments over all 64 banks.
+template <int D>
+__device__ __forceinline__ constexpr int vswz(int row) {
+    return 4 * ((row / Geo<D>::RPL) % (Geo<D>::SEGS / 4));
+}
 
 // Key order of the q.k product. Row n of the 32x32 MFMA's K operand holds key
 // sigma(n) of the sub-step (bits 2 and 3 of n swapped). The result registers
@@ -420,152 +434,179 @@ __device__ __forceinline__ void lds_barrier() {
 // middle outwards balanced no better and shared less.)
 __device__ __forceinline__ int32_t rank_to_qblock(int32_t rank) { return rank; }
 
-// Buffer descriptor over one head's K or V slab (raw, unswizzled, 32-bit data).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t *base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), static_cast<short>(0),
-                                             static_cast<int>(bytes), 0x00020000);
+// Buffer descriptor over `bytes` bytes at `base` (raw, unswizzled, 32-bit
+// data), in scalar registers.
+__device__ __forceinline__ u32x4 head_rsrc(const void *base, int64_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane(uint32_t(b));
+    r[1] = __builtin_amdgcn_readfirstlane(uint32_t(b >> 32) & 0xffffu);
+    r[2] = uint32_t(bytes);
+    r[3] = 0x00020000u;
+    return r;
+}
+
+// Compile-time loop: f(integral_constant<int, I>) for I = B .. E - 1.
+template <int B, int E>
+struct Unroll {
+    template <typename F>
+    static __device__ __forceinline__ void run(F &&f) {
+        if constexpr (B < E) {
+            f(std::integral_constant<int, B>{});
+            Unroll<B + 1, E>::run(f);
+        }
+    }
+};
+
+// One direct global -> LDS load of 16 bytes per lane (buffer_load_dwordx4
+// ... lds): lane l's bytes land at lds + 16 l. Written as an instruction of
+// its own: the compiler cannot tell that these LDS writes never alias the
+// LDS reads between them and would otherwise wait for every load in flight
+// before each such read, turning the prefetch synchronous. The load has no
+// register result; the walk waits for it explicitly (vmcnt) before the
+// barrier that publishes its stage.
+__device__ __forceinline__ void load_lds16(u32x4 rs, char *lds, int32_t voff, int32_t soff) {
+    const uint32_t m0 = uint32_t(reinterpret_cast<uintptr_t>((lds_void *)lds));
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(rs), "s"(soff)
+                 : "memory", "m0");
+}
+
+// The same for 4 bytes per lane (lane l's bytes land at lds + 4 l).
+__device__ __forceinline__ void load_lds4(u32x4 rs, char *lds, int32_t voff) {
+    const uint32_t m0 = uint32_t(reinterpret_cast<uintptr_t>((lds_void *)lds));
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(rs)
+                 : "memory", "m0");
 }
 
 // One workgroup per (batch, head, query block): 8 wavefronts, two per SIMD,
 // each owning a tile of 32 query rows (Q fragments and the fp32 output
-// accumulators in registers). Stages of 64 keys rotate through three LDS
-// buffers.
+// accumulators in registers). Stages of 64 keys go straight from global
+// memory into four rotating LDS buffers, three stages ahead.
 template <int D>
 struct AttnKernel {
     using G = Geo<D>;
     static constexpr int NW = 8;
     static constexpr int THREADS = 64 * NW;
-    static constexpr int KL = 64 * G::SEGS / THREADS;   // 16-byte K (and V) loads per thread and stage
-    static constexpr int RPI = 64 / G::SEGS;            // V rows per wave-wide load
-    static constexpr int NBUF = 3;
-    static constexpr int LDS_BYTES = NBUF * G::STAGE;
+    static constexpr int KL = 64 * G::SEGS / THREADS;   // 1 KB K (and V) load instructions per wave and stage
+    static constexpr int LPS = 2 * KL;                  // load instructions per wave and stage
+    static constexpr int RPI = 64 / G::SEGS;            // V rows per load instruction
+    static constexpr int NBUF = 4;
+    static constexpr int TAB_BYTES = 512;               // per wavefront: two 64-entry tile tables
+    static constexpr int LDS_BYTES = NBUF * G::STAGE + NW * TAB_BYTES;
     static_assert(KL >= 1 && NW * KL * 64 == 64 * G::SEGS, "loads cover the stage");
-
-    // Global -> register staging of one stage.
-    struct Stage {
-        u32x4 k[KL], v[KL];
-    };
+    static_assert(2 * KL * RPI == 16, "two wavefronts load one 16-key tile");
 
     // The row's 16-key tiles as a table in one vector register: lane l of
     // `cur` holds the byte offset of tile 64 m + l of the row's key list, so
     // a wavefront takes its stage tile's offset with one v_readlane (stage
-    // s, tile j of the stage: lane 4 (s % 16) + j). The next 64 tiles' block
-    // columns (one vector load, lane l: list entry e0 + t / hpb) and
-    // tile-in-block positions are fetched when a table is taken into use, 16
-    // stages before they are needed. Tiles past the row end repeat the row's last tile: they are
-    // loaded but never weighted. (Walking the list with a scalar cursor and
-    // scalar loads cost about 60 scalar instructions per stage and a wait on
-    // the scalar loads that also held the stage's LDS stores.)
+    // s, tile j of the stage: lane 4 (s % 16) + j). The block columns of the
+    // next 64 tiles (lane l: list entry e0 + t / hpb) are fetched when a
+    // table is taken into use, 16 stages before they are needed, straight
+    // into one of two per-wavefront LDS slots (loaded like the stages, so
+    // the stage barriers' waits cover them); the tile-in-block positions are
+    // computed then. Tiles past the row end repeat the row's last tile: they
+    // are loaded but never weighted.
     struct TileTab {
-        int32_t cur, c, j;
+        int32_t cur, j;
+        char *slots;
     };
-    static __device__ __forceinline__ void tab_fetch(const gint32 *col, int32_t e0, int32_t nquart, int hpb,
-                                                     int32_t m, TileTab &tt) {
-        int32_t t = 64 * m + int32_t(threadIdx.x & 63);
-        t = t < nquart ? t : nquart - 1;
+    static __device__ __forceinline__ int32_t tab_tile(int32_t nquart, int32_t m) {
+        const int32_t t = 64 * m + int32_t(threadIdx.x & 63);
+        return t < nquart ? t : nquart - 1;
+    }
+    static __device__ __forceinline__ void tab_issue(u32x4 crs, int32_t e0, int32_t nquart, int hpb, int32_t m,
+                                                     TileTab &tt) {
+        const int32_t t = tab_tile(nquart, m);
         const int32_t blk = int32_t(uint32_t(t) / uint32_t(hpb));
         tt.j = t - blk * hpb;
-        tt.c = col[e0 + blk];
+        load_lds4(crs, tt.slots + (m & 1) * 256, (e0 + blk) * 4);
+    }
+    // Table 0 from a plain load (nothing else is in flight yet), table 1
+    // requested.
+    static __device__ __forceinline__ void tab_init(const gint32 *col, u32x4 crs, int32_t e0, int32_t nquart,
+                                                    int hpb, int bk, char *slots, TileTab &tt) {
+        tt.slots = slots;
+        const int32_t t = tab_tile(nquart, 0);
+        const int32_t blk = int32_t(uint32_t(t) / uint32_t(hpb));
+        tt.cur = (col[e0 + blk] * bk + 16 * (t - blk * hpb)) * (D * 2);
+        tab_issue(crs, e0, nquart, hpb, 1, tt);
     }
     static __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-    // Byte offset of this wavefront's tile (wave_tile()) in stage `sig`
-    // (wave-uniform, counted from 0); advances sig.
-    static __device__ __forceinline__ int32_t next_src(const gint32 *col, TileTab &tt, int32_t &sig, int32_t e0,
+    // Byte offset of this wavefront's tile (tile wave / 2 of the stage) in
+    // stage `sig` (wave-uniform, counted from 0); advances sig.
+    static __device__ __forceinline__ int32_t next_src(u32x4 crs, TileTab &tt, int32_t &sig, int32_t e0,
                                                        int32_t nquart, int hpb, int bk) {
-        if ((sig & 15) == 0) {
-            tt.cur = (tt.c * bk + 16 * tt.j) * (D * 2);
-            tab_fetch(col, e0, nquart, hpb, sig / 16 + 1, tt);
+        if ((sig & 15) == 0 && sig > 0) {
+            const int32_t m = sig / 16;
+            const int32_t c = *reinterpret_cast<const int32_t *>(tt.slots + (m & 1) * 256 + 4 * (threadIdx.x & 63));
+            tt.cur = (c * bk + 16 * tt.j) * (D * 2);
+            tab_issue(crs, e0, nquart, hpb, m + 1, tt);
         }
-        const int i = 4 * (sig & 15) + wave_tile(wave_id());
+        const int i = 4 * (sig & 15) + wave_id() / 2;
         ++sig;
         return __builtin_amdgcn_readlane(tt.cur, i);
     }
 
-    // Stage loads. K: wave-wide instruction X = KL w + x covers 16 keys of one
-    // tile and 4 segments (lane l: key l % 16, segment 4 (X % (SEGS / 4)) +
-    // l / 16), so in the segment-major LDS layout the 16 lanes of a quarter
-    // wave write 16 consecutive 16-byte slots. V: instruction X covers whole
-    // rows RPI X .. RPI X + RPI - 1 (lane l: row RPI X + l / SEGS, segment
-    // l % SEGS). Each instruction stays inside one 16-key tile, so the tile
-    // index follows from the wave index alone and the tile's offset is a
-    // scalar operand of the buffer load. All of a wavefront's loads fall in
-    // one tile, wave_tile(w).
-    static constexpr int k_tile(int w, int x) { return (KL * w + x) / (G::SEGS / 4); }
-    static constexpr int k_segq(int w, int x) { return (KL * w + x) % (G::SEGS / 4); }
-    static constexpr int v_row(int w, int x) { return RPI * (KL * w + x); }
-    static constexpr int wave_tile(int w) { return w / (NW / 4); }
-    static constexpr bool one_tile_per_wave() {
-        for (int w = 0; w < NW; ++w)
-            for (int x = 0; x < KL; ++x)
-                if (k_tile(w, x) != wave_tile(w) || v_row(w, x) / 16 != wave_tile(w)) return false;
-        return true;
-    }
-    static_assert(NW % 4 == 0 && one_tile_per_wave(), "a wavefront's stage loads stay in one 16-key tile");
-
+    // Direct global -> LDS loads of one stage: wavefronts 2t and 2t + 1 load
+    // 16-key tile t (K and V; the tile's offset `src` is the scalar offset of
+    // the buffer loads), instructions X = KL (w % 2) + x of the tile's 2 KL.
+    // K instruction X: lane l loads key l % 16, segment 4 X + l / 16, which
+    // is slot 64 X + l of the tile's segment-major layout. V instruction X:
+    // lane l loads row RPI X + l / SEGS of the tile into slot l % SEGS, i.e.
+    // segment (l % SEGS) ^ vswz(row). Each instruction reads 64-byte (K) or
+    // whole-row (V) runs of global memory.
     struct LoadOffsets {
-        int32_t k[KL], v[KL];      // bytes inside a 16-key tile
+        int32_t k, v;              // per-lane bytes of instruction 0 inside a 16-key global tile
     };
     static __device__ __forceinline__ LoadOffsets load_offsets() {
-        const int l = threadIdx.x & 63, w = wave_id();
+        const int l = threadIdx.x & 63;
         LoadOffsets lo;
-#pragma unroll
-        for (int x = 0; x < KL; ++x) {
-            lo.k[x] = ((l % 16) * D + (4 * k_segq(w, x) + l / 16) * 8) * 2;
-            lo.v[x] = ((v_row(w, x) % 16 + l / G::SEGS) * D + (l % G::SEGS) * 8) * 2;
-        }
+        lo.k = (l % 16) * G::ROWB + (l / 16) * 16;
+        const int rt = l / G::SEGS;                            // row inside the instruction's rows
+        lo.v = rt * G::ROWB + ((l % G::SEGS) ^ vswz<D>(rt)) * 16;   // vswz(RPI X + rt) = vswz(rt)
         return lo;
     }
-
-    static __device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
-                                                      const LoadOffsets &lo, int32_t src, Stage &st) {
+    static __device__ __forceinline__ void issue_stage(u32x4 krs, u32x4 vrs, const LoadOffsets &lo, int32_t src,
+                                                       char *stage) {
+        const int w = wave_id(), t = w / 2;
+        char *kt = stage + (t / 2) * G::SUB_BYTES + (t % 2) * G::TILE_K;
+        char *vt = stage + (t / 2) * G::SUB_BYTES + G::SUB_K + 16 * (t % 2) * G::ROWB;
+        const int x0 = KL * (w % 2);
 #pragma unroll
         for (int x = 0; x < KL; ++x) {
-            st.k[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, lo.k[x], src, 0));
-            st.v[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, lo.v[x], src, 0));
+            load_lds16(krs, kt + 1024 * (x0 + x), lo.k, src + 64 * (x0 + x));
+            load_lds16(vrs, vt + 1024 * (x0 + x), lo.v, src + RPI * (x0 + x) * G::ROWB);
         }
     }
 
-    struct StoreOffsets {
-        int32_t k[KL], v[KL];      // bytes inside an LDS stage
-    };
-    static __device__ __forceinline__ StoreOffsets store_offsets() {
-        const int l = threadIdx.x & 63, w = wave_id();
-        StoreOffsets so;
-#pragma unroll
-        for (int x = 0; x < KL; ++x) {
-            const int key = 16 * k_tile(w, x) + l % 16;
-            so.k[x] = (key / 32) * G::SUB_BYTES + ((4 * k_segq(w, x) + l / 16) * 32 + key % 32) * 16;
-            const int row = v_row(w, x) + l / G::SEGS;
-            so.v[x] = (row / 32) * G::SUB_BYTES + G::SUB_K + (row % 32) * G::VRS + (l % G::SEGS) * 16;
-        }
-        return so;
-    }
-
-    static __device__ __forceinline__ void store_stage(char *stage, const StoreOffsets &so, const Stage &st) {
-#pragma unroll
-        for (int x = 0; x < KL; ++x) {
-            *reinterpret_cast<u32x4 *>(stage + so.k[x]) = st.k[x];
-            *reinterpret_cast<u32x4 *>(stage + so.v[x]) = st.v[x];
-        }
-    }
-
-    // LDS byte offsets of this lane's fragment reads relative to a sub-step;
-    // the k-step / column tile adds an immediate.
-    //   K: lane (n, h) reads key sigma(n), segment 2 ks + h.
+    // LDS byte offsets of this lane's fragment reads relative to a sub-step.
+    //   K: lane (n, h) reads key sigma(n) (tile n / 16), segment 2 ks + h;
+    //      the k-step adds an immediate.
     //   V: transposing reads, per 16-lane group four rows of 16 d: lane a of
     //      the group addresses row a / 4 and d 4 (a % 4) of the group's block
-    //      and receives d = its own column, four consecutive keys.
+    //      and receives d = its own column, four consecutive keys. The column
+    //      tile dt changes the permuted segment per lane (one offset per dt);
+    //      the k-step and the second read (rows + 4) add immediates.
     struct ReadOffsets {
-        int32_t k, v;
+        int32_t k, v[G::DT];
     };
     static __device__ __forceinline__ ReadOffsets read_offsets() {
         const int lane = threadIdx.x & 63;
         const int n = lane & 31, h = lane >> 5;
-        const int a = lane & 15, n0 = 16 * ((lane >> 4) & 1);
+        const int a = lane & 15, g16 = (lane >> 4) & 1;
         ReadOffsets ro;
-        ro.k = (h * 32 + sigma(n)) * 16;
-        ro.v = G::SUB_K + (8 * h + a / 4) * G::VRS + (n0 + 4 * (a % 4)) * 2;
+        ro.k = (n / 16) * G::TILE_K + h * 256 + (sigma(n) % 16) * 16;
+        const int row = 8 * h + a / 4;
+#pragma unroll
+        for (int dt = 0; dt < G::DT; ++dt) {
+            const int seg = 4 * dt + 2 * g16 + (a % 4) / 2;
+            ro.v[dt] = G::SUB_K + row * G::ROWB + (seg ^ vswz<D>(row)) * 16 + 8 * (a % 2);
+        }
         return ro;
     }
 
@@ -573,7 +614,7 @@ struct AttnKernel {
     // d = 16 ks + 8 h .. + 8 for each k-step ks.
     static __device__ __forceinline__ void read_k(const char *sub, const ReadOffsets &ro, bf16x8 (&ka)[G::KS]) {
 #pragma unroll
-        for (int ks = 0; ks < G::KS; ++ks) ka[ks] = *reinterpret_cast<const bf16x8 *>(sub + ro.k + ks * 1024);
+        for (int ks = 0; ks < G::KS; ++ks) ka[ks] = *reinterpret_cast<const bf16x8 *>(sub + ro.k + ks * 512);
     }
 
     // V^T fragments (A operand of p.v): lane (n, h) holds d = 32 dt + n and
@@ -584,9 +625,9 @@ struct AttnKernel {
         for (int dt = 0; dt < G::DT; ++dt)
 #pragma unroll
             for (int ks = 0; ks < PVK; ++ks) {
-                const char *vp = sub + ro.v + 16 * ks * G::VRS + 64 * dt;
+                const char *vp = sub + ro.v[dt] + 16 * ks * G::ROWB;
                 const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vp));
-                const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vp + 4 * G::VRS));
+                const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vp + 4 * G::ROWB));
                 va[dt][ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
             }
     }
@@ -681,12 +722,26 @@ struct AttnKernel {
         }
     }
 
-    // The block-list walk in stages of 64 keys. Stage s sits in LDS buffer
-    // s % 3; while stage s is computed, stage s + 1 is already in LDS (the
-    // scores of the next sub-step are computed ahead), stage s + 2 is stored
-    // from registers and stage s + 3 is in flight from global memory. One
-    // barrier per stage. NG = 0: a wavefront without rows still stages K/V
-    // and meets every barrier.
+    // Wait until at most `vm` of this wavefront's global loads are
+    // outstanding (loads complete in order) and its LDS accesses are done,
+    // then meet the workgroup at the barrier.
+    template <int vm>
+    static __device__ __forceinline__ void stage_barrier() {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt((vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (0 << 8));
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
+
+    // The block-list walk in stages of 64 keys (two sub-steps), loaded
+    // straight into LDS three stages ahead. Stage s sits in buffer s % 4.
+    // Its sub-steps 2s and 2s + 1 read K of 2s + 1 and 2s + 2 (the latter in
+    // stage s + 1) and V of their own. The barrier after sub-step 2s first
+    // waits for this wavefront's loads of stage s + 1 (only those of stage
+    // s + 2 may still be in flight), so it publishes stage s + 1; every
+    // wavefront has then also finished stage s - 1, whose buffer receives
+    // stage s + 3. NG = 0: a wavefront without rows still loads its share
+    // of every stage and meets every barrier.
     template <int NG, bool ONLINE>
     static __device__ __forceinline__ void walk(const AttnParams &p, char *smem, const uint16_t *kh,
                                                 const uint16_t *vh, int32_t e0, int32_t nquart, Rows &rw) {
@@ -695,57 +750,56 @@ struct AttnKernel {
         const int hpb = p.block_k / 16;
         const gint32 *col = (const gint32 *)(p.col_idx);
         const int64_t slab = int64_t(p.seq_len) * D * 2;
-        const __amdgpu_buffer_rsrc_t krs = head_rsrc(kh, slab), vrs = head_rsrc(vh, slab);
+        const u32x4 krs = head_rsrc(kh, slab), vrs = head_rsrc(vh, slab);
+        const u32x4 crs = head_rsrc(p.col_idx, int64_t(e0 + (nquart - 1) / hpb + 1) * 4);
         const LoadOffsets lo = load_offsets();
-        const StoreOffsets so = store_offsets();
         const ReadOffsets ro = read_offsets();
         TileTab tt;
-        tab_fetch(col, e0, nquart, hpb, 0, tt);
+        tab_init(col, crs, e0, nquart, hpb, p.block_k, smem + NBUF * G::STAGE + wave_id() * TAB_BYTES, tt);
         int32_t sig = 0;
-        Stage st;
-        char *const b0 = smem, *const b1 = smem + G::STAGE, *const b2 = smem + 2 * G::STAGE;
+        char *const b0 = smem, *const b1 = smem + G::STAGE, *const b2 = smem + 2 * G::STAGE,
+                    *const b3 = smem + 3 * G::STAGE;
 
-        load_stage(krs, vrs, lo, next_src(col, tt, sig, e0, nquart, hpb, p.block_k), st);
-        store_stage(b0, so, st);
-        load_stage(krs, vrs, lo, next_src(col, tt, sig, e0, nquart, hpb, p.block_k), st);
-        store_stage(b1, so, st);
-        load_stage(krs, vrs, lo, next_src(col, tt, sig, e0, nquart, hpb, p.block_k), st);
-        int32_t nxt = next_src(col, tt, sig, e0, nquart, hpb, p.block_k);
-        lds_barrier();
+        // stages 0 .. 2 (those that exist) in flight, 0 and 1 complete
+        issue_stage(krs, vrs, lo, next_src(crs, tt, sig, e0, nquart, hpb, p.block_k), b0);
+        if (nst > 1) issue_stage(krs, vrs, lo, next_src(crs, tt, sig, e0, nquart, hpb, p.block_k), b1);
+        if (nst > 2) {
+            issue_stage(krs, vrs, lo, next_src(crs, tt, sig, e0, nquart, hpb, p.block_k), b2);
+            stage_barrier<LPS>();
+        } else {
+            stage_barrier<0>();
+        }
         if constexpr (NG > 0) {
             bf16x8 ka[G::KS];
             read_k(b0, ro, ka);
             rw.s = qk(ka, rw.qf);
         }
 
-        // Every stage but the last: two full sub-steps, each with a next one.
-        // The loop is unrolled by three so that every LDS address is a fixed
-        // per-lane offset plus an immediate.
-        auto body = [&](char *bc, char *bn, char *bs) {
-            store_stage(bs, so, st);
-            load_stage(krs, vrs, lo, nxt, st);
-            nxt = next_src(col, tt, sig, e0, nquart, hpb, p.block_k);
-            step<NG, ONLINE, false, true>(bc, bc + G::SUB_BYTES, ro, rw, p.c);
-            step<NG, ONLINE, false, true>(bc + G::SUB_BYTES, bn, ro, rw, p.c);
-            lds_barrier();
-        };
+        // stage s but the last: two full sub-steps, each with a next one,
+        // the barrier between them, then the loads of stage s + 3 (if it
+        // exists)
         int s = 0;
-        for (; s + 3 <= nst - 1; s += 3) {
-            body(b0, b1, b2);
-            body(b1, b2, b0);
-            body(b2, b0, b1);
-        }
-        if (s < nst - 1) {
-            body(b0, b1, b2);
+        auto body = [&](char *bc, char *bn, char *bl) {
+            step<NG, ONLINE, false, true>(bc, bc + G::SUB_BYTES, ro, rw, p.c);
+            stage_barrier<LPS>();
+            if (s + 3 < nst) issue_stage(krs, vrs, lo, next_src(crs, tt, sig, e0, nquart, hpb, p.block_k), bl);
+            step<NG, ONLINE, false, true>(bc + G::SUB_BYTES, bn, ro, rw, p.c);
             ++s;
-            if (s < nst - 1) {
-                body(b1, b2, b0);
-                ++s;
-            }
+        };
+        // stage s uses buffer s % 4; the loop is unrolled by four so that
+        // every LDS address is a fixed per-lane offset plus an immediate
+        while (s + 4 <= nst - 1) {
+            body(b0, b1, b3);
+            body(b1, b2, b0);
+            body(b2, b3, b1);
+            body(b3, b0, b2);
         }
+        if (s < nst - 1) body(b0, b1, b3);
+        if (s < nst - 1) body(b1, b2, b0);
+        if (s < nst - 1) body(b2, b3, b1);
         // the last stage: 1 to 4 valid 16-key tiles
-        const int r3 = (nst - 1) % 3;
-        char *const b = r3 == 0 ? b0 : (r3 == 1 ? b1 : b2);
+        const int r4 = s % 4;
+        char *const b = r4 == 0 ? b0 : (r4 == 1 ? b1 : (r4 == 2 ? b2 : b3));
         switch (nquart - 4 * (nst - 1)) {
             case 1: step<NG, ONLINE, true, false>(b, b, ro, rw, p.c); break;
             case 2: step<NG, ONLINE, false, false>(b, b, ro, rw, p.c); break;
@@ -758,6 +812,8 @@ struct AttnKernel {
                 step<NG, ONLINE, false, false>(b + G::SUB_BYTES, b, ro, rw, p.c);
                 break;
         }
+        // no load into LDS may still be in flight when the buffers are reused
+        __builtin_amdgcn_s_waitcnt((0) | (0 << 14) | (7 << 4) | (15 << 8));   // vmcnt(0)
     }
 
     // This wavefront's tile: rows row0 .. row0 + nvalid - 1 (nvalid 16 or 32)
@@ -872,7 +928,9 @@ struct AttnKernel {
     template <bool CENTRED>
     static __device__ void run(const AttnParams &p) {
         extern __shared__ __attribute__((aligned(16))) char smem[];
-        float *red = reinterpret_cast<float *>(smem + 2 * G::STAGE);   // stage buffer 2 is free until the walk
+        // stage buffer 3 receives its first load only after every wavefront has
+        // passed the walk's first barrier, so it can hold this reduction
+        float *red = reinterpret_cast<float *>(smem + 3 * G::STAGE);
         const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
         // XCD-aware order: consecutive workgroup ids go to different XCDs, so
