@@ -34,11 +34,12 @@
 //   O^T += V^T P^T    bf16 MFMA 32x32x16, V^T read from row-major V in LDS
 //                     with the transposing LDS reads
 // The scores of sub-step j + 1 are computed in the same step as the weights
-// and p.v of sub-step j. Heads whose bound is too loose run the same walk
-// with the standard running max and rescale instead ([vi:Softmax], Fig. 4),
-// chosen by a branch that is uniform over the workgroup; that tile is a
-// separate, non-inlined function, so its registers do not crowd the bound
-// path's, and it rescales only when a row's max has grown by more than 2^8.
+// and p.v of sub-step j. K and V stages go from global memory straight into
+// LDS (buffer loads with the LDS flag), three stages ahead. Heads whose
+// bound is too loose run the same walk with the standard running max and
+// rescale instead ([vi:Softmax], Fig. 4), chosen by a branch that is uniform
+// over the workgroup; it rescales only when a row's max has grown by more
+// than 2^8.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -55,9 +56,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Device data in the global address space: loads through it are vector
-// (global_load) loads even inside a non-inlined function, whose pointer
-// arguments are otherwise generic (flat loads, which also count on the LDS
-// counter and so coarsen the LDS waits).
+// (global_load) loads, never generic (flat) ones, which also count on the
+// LDS counter and so coarsen the LDS waits.
 typedef __attribute__((address_space(1))) const int32_t gint32;
 typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
 typedef short v8s __attribute__((__vector_size__(8 * sizeof(short))));
@@ -893,38 +893,6 @@ struct AttnKernel {
         }
     }
 
-    // The online-fallback tile as a function of its own (not inlined): its
-    // register allocation then does not weigh on the bound path's. Its
-    // arguments arrive in vector registers; the wave-uniform ones are moved
-    // back to scalar registers so that the walk's stage offsets, LDS
-    // addresses and loop control stay scalar.
-    static __device__ __forceinline__ int32_t uni(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
-    static __device__ __forceinline__ int64_t uni64(int64_t x) {
-        const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int32_t(uint64_t(x) & 0xffffffffu)));
-        const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int32_t(uint64_t(x) >> 32)));
-        return int64_t((uint64_t(hi) << 32) | lo);
-    }
-    template <typename T>
-    static __device__ __forceinline__ T *uniptr(T *x) { return reinterpret_cast<T *>(uni64(int64_t(x))); }
-
-    template <int NG>
-    static __device__ __attribute__((noinline)) void tile_online(const uint16_t *q, uint16_t *o, const int32_t *col_idx,
-                                                                 float c, int32_t seq_len, int32_t block_k,
-                                                                 int64_t head_row0, int32_t row0, int32_t nvalid,
-                                                                 const uint16_t *kh, const uint16_t *vh, int32_t e0,
-                                                                 int32_t nquart) {
-        extern __shared__ __attribute__((aligned(16))) char smem[];
-        AttnParams lp = {};
-        lp.q = uniptr(q);
-        lp.o = uniptr(o);
-        lp.col_idx = uniptr(col_idx);
-        lp.c = __uint_as_float(uint32_t(uni(int32_t(__float_as_uint(c)))));
-        lp.seq_len = uni(seq_len);
-        lp.block_k = uni(block_k);
-        tile<NG, false>(lp, smem, uni64(head_row0), uni(row0), uni(nvalid), uniptr(kh), uniptr(vh), uni(e0),
-                        uni(nquart), true, 0.0f, nullptr);
-    }
-
     template <bool CENTRED>
     static __device__ void run(const AttnParams &p) {
         extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -971,11 +939,9 @@ struct AttnKernel {
             const int nvalid = p.block_q - 32 * my < 32 ? p.block_q - 32 * my : 32;
             if (online) {
                 if (my < ntiles)
-                    tile_online<1>(p.q, p.o, p.col_idx, p.c, p.seq_len, p.block_k, head_row0, row0, nvalid, kh, vh,
-                                   e0, nquart);
+                    tile<1, false>(p, smem, head_row0, row0, nvalid, kh, vh, e0, nquart, true, 0.0f, nullptr);
                 else
-                    tile_online<0>(p.q, p.o, p.col_idx, p.c, p.seq_len, p.block_k, head_row0, row0, nvalid, kh, vh,
-                                   e0, nquart);
+                    tile<0, false>(p, smem, head_row0, row0, nvalid, kh, vh, e0, nquart, true, 0.0f, nullptr);
             } else if (my < ntiles) {
                 tile<1, CENTRED>(p, smem, head_row0, row0, nvalid, kh, vh, e0, nquart, false, mk, mu);
             } else {
