@@ -63,18 +63,30 @@ PRE_SOURCE = os.path.join(ROOT, "frame_windowed_block_amd", "csrc", "fsa_preattn
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def kernel_code_digest(source: str = KERNEL_SOURCE) -> str:
+    """sha256 of the kernel source with its // comments, trailing blanks and
+    empty lines removed: the code the counters were taken on, not its prose."""
+    import hashlib
+    import re
+    lines = []
+    with open(source, encoding="utf-8") as fh:
+        for line in fh:
+            code = re.sub(r"//.*$", "", line.rstrip("\n")).rstrip()
+            if code:
+                lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def measured_traffic(kernel: str, workload: str, source: str = KERNEL_SOURCE):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    passes (copy-calibrated), or None when they were taken on other kernel source."""
-    import hashlib
+    passes (copy-calibrated), or None when they were taken on other kernel code."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)[kernel][workload]
-        with open(source, "rb") as fh:
-            sha = hashlib.sha256(fh.read()).hexdigest()
+        digest = kernel_code_digest(source)
     except (OSError, KeyError, ValueError):
         return None
-    return rec["traffic_bytes"] if rec.get("kernel_source_sha256") == sha else None
+    return rec["traffic_bytes"] if rec.get("kernel_code_sha256") == digest else None
 
 
 def preroll(step, ms: float) -> tuple[float, int]:

@@ -10,8 +10,9 @@
 // fsa_bounds runs two kernels (four with key centring, which first reduces the
 // keys of each head to their mean in two fixed-order kernels). norms_kernel
 // streams q and k once (the HBM-bound part): it writes ||q_i|| per row and,
-// per key block, the largest ||k_j|| (of k_j - mean when centred) ("a small
-// array of precomputed norms", [vi:Softmax]). bound_reduce_kernel
+// per key block, the largest ||k_j|| (of k_j - mean when centred): the norms,
+// computed ahead of the attention pass, that its bound is built from
+// ([vi:Softmax]). bound_reduce_kernel
 // then derives, per query block, scale * max ||q_i|| * max kmax over the
 // block's active key blocks, folds it into the head's largest row bound, and
 // the last block of each head writes the head's eligibility ([vi:Softmax]:
@@ -464,7 +465,8 @@ struct Unroll {
 // LDS reads between them and would otherwise wait for every load in flight
 // before each such read, turning the prefetch synchronous. The load has no
 // register result; the walk waits for it explicitly (vmcnt) before the
-// barrier that publishes its stage.
+// barrier that publishes its stage. The asm sets M0 (the LDS base of the
+// copy); nothing else in these kernels keeps a value in M0.
 __device__ __forceinline__ void load_lds16(u32x4 rs, char *lds, int32_t voff, int32_t soff) {
     const uint32_t m0 = uint32_t(reinterpret_cast<uintptr_t>((lds_void *)lds));
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"

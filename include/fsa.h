@@ -12,7 +12,7 @@
  *                  neighbouring frames plus one global reference frame; block
  *                  sizes are multiples of 16 that divide a frame, so every
  *                  block is fully inside or fully outside the mask.
- *   fsa_bounds     the small precomputed norm array behind the softmax bound
+ *   fsa_bounds     the norms, computed ahead of attention, that the softmax bound is built from
  *                  (section "Giải phóng Softmax"): per-row query norms,
  *                  per-key-block largest key norms, and the per-head check of
  *                  whether the bound is tight enough to use; optionally with

@@ -26,7 +26,7 @@ window of neighbouring frames plus one global reference frame [vi:Mask]; the
 tile grid is cut in steps of 16 tokens that divide a frame, so every block is
 fully inside or fully outside the mask [vi:Mask, Fig. 3]; and the running max
 of online softmax is replaced by a per-row Cauchy-Schwarz bound built from
-precomputed norms, which leaves the output unchanged in exact arithmetic
+norms computed beforehand, which leaves the output unchanged in exact arithmetic
 [vi:Softmax]. The method therefore reaches exactly masked softmax attention,
 and this oracle is that definition written out: dense scores over all keys,
 the frame mask applied, a standard max-subtract softmax, in fp64.
