@@ -18,7 +18,8 @@ between two device synchronisations. Prints ONE JSON line:
   (the event after it also marks the plan buffer free for reuse); the
   bounds pass is bracketed by its own events on every fourth timed step
   only, since each event recorded between two kernels holds the stream for
-  several microseconds;
+  several microseconds, and is also timed on its own after the timed steps
+  (bounds.alone_*: 60 calls back to back over the rotating input copies);
 * cpu_baseline: the fp64 oracle (not tuned) timed on four heads of the same
   workload on the host cores, scaled to the same unit;
 * check: the last timed step's output on those four heads against that oracle
@@ -56,6 +57,8 @@ if ROOT not in sys.path:
 METRIC = "effective TFLOP/s on active blocks + % of bf16 MFMA peak, 25k-token SR attn"
 # fsa_bounds is bracketed by timing events on every BOUNDS_EVERY-th timed step
 BOUNDS_EVERY = 4
+# after the timed steps, this many bounds calls run back to back on their own
+BOUNDS_ALONE = 60
 PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "frame_windowed_block_amd", "csrc", "fsa_kernels.hip")
@@ -559,6 +562,19 @@ def main():
     attn_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     bnd_ms = np.array([e[0].elapsed_time(e[1]) for i, e in enumerate(evs) if i % BOUNDS_EVERY == 0])
 
+    # the bounds pass on its own, after the timed steps: BOUNDS_ALONE calls
+    # back to back over the rotating input copies, one event pair around them
+    # all (no event between its two kernels or before the attention kernel)
+    torch.cuda.synchronize()
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record(stream)
+    for i in range(BOUNDS_ALONE):
+        bq_, bk_, _ = inputs[i % len(inputs)]
+        fsa.bounds(dplans[0], bq_, bk_, wl.scale, 0.0, 0, 0, qn, km, el, bm, stream=stream, kmean=mu)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    bounds_alone_ms = b0.elapsed_time(b1) / BOUNDS_ALONE
+
     flops = plan_flops(info0, bsz, heads, d)
     ms_per_step = total_ms / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -623,6 +639,9 @@ def main():
             "mean_ms": round(float(bnd_ms.mean()), 5),
             "median_ms": round(float(np.median(bnd_ms)), 5),
             "gbps": round(bounds_bytes / (float(bnd_ms.mean()) * 1e-3) / 1e9, 1),
+            "alone_calls": BOUNDS_ALONE,
+            "alone_mean_ms": round(bounds_alone_ms, 5),
+            "alone_gbps": round(bounds_bytes / (bounds_alone_ms * 1e-3) / 1e9, 1),
             "input_copies": len(inputs),
             "peak_gbps": PEAK_HBM_GBPS,
             "algorithmic_bytes": bounds_bytes,

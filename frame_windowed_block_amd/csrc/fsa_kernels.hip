@@ -318,10 +318,10 @@ __global__ __launch_bounds__(256) void norms_kernel(NormsParams p) {
 // --------------------------------------------------------------------------
 struct ReduceParams {
     const float *qnorm, *kmax;
-    const int32_t *row_ptr, *col_idx;
     int32_t *eligible;
     float *bmax;
     int32_t heads, seq_len, h0, hc, block_q, n_qb, n_kb, chunks;
+    int32_t frames, tokens_per_frame, window, ref_frame, block_k;
     float scale, limit;
 };
 
@@ -343,10 +343,23 @@ __global__ __launch_bounds__(256) void bound_reduce_kernel(ReduceParams p) {
         float qm = 0.0f;
 #pragma unroll 8
         for (int i = sl; i < p.block_q; i += 16) qm = nan_max(qm, qn[i]);
-        const int32_t e0 = p.row_ptr[qb], e1 = p.row_ptr[qb + 1];
+        // the block's active key blocks, from the plan's frame rule: every
+        // block of the frames in the window, clipped at the ends, and of the
+        // reference frame (the same list the plan's CSR holds; computed
+        // here so that the kmax loads do not wait for list loads)
+        const int32_t kbpf = p.tokens_per_frame / p.block_k;
+        const int32_t f = qb / (p.tokens_per_frame / p.block_q);
+        const int32_t g0 = f - p.window > 0 ? f - p.window : 0;
+        const int32_t g1 = f + p.window < p.frames - 1 ? f + p.window : p.frames - 1;
+        const float *km_head = p.kmax + hb * p.n_kb;
         float km = 0.0f;
 #pragma unroll 4
-        for (int32_t e = e0 + sl; e < e1; e += 16) km = nan_max(km, p.kmax[hb * p.n_kb + p.col_idx[e]]);
+        for (int32_t kb = g0 * kbpf + sl; kb < (g1 + 1) * kbpf; kb += 16) km = nan_max(km, km_head[kb]);
+        if (p.ref_frame < g0 || p.ref_frame > g1) {
+#pragma unroll 2
+            for (int32_t kb = p.ref_frame * kbpf + sl; kb < (p.ref_frame + 1) * kbpf; kb += 16)
+                km = nan_max(km, km_head[kb]);
+        }
 #pragma unroll
         for (int off = 8; off >= 1; off >>= 1) {
             qm = nan_max(qm, __shfl_xor(qm, off));
@@ -1034,8 +1047,6 @@ int launch_bounds(const BoundsLaunch &a) {
     ReduceParams rp;
     rp.qnorm = a.qnorm;
     rp.kmax = a.kmax;
-    rp.row_ptr = a.row_ptr;
-    rp.col_idx = a.col_idx;
     rp.eligible = a.eligible;
     rp.bmax = a.bmax;
     rp.heads = a.heads;
@@ -1045,6 +1056,11 @@ int launch_bounds(const BoundsLaunch &a) {
     rp.block_q = pl.block_q;
     rp.n_qb = pl.n_qblocks;
     rp.n_kb = pl.n_kblocks;
+    rp.frames = pl.frames;
+    rp.tokens_per_frame = pl.tokens_per_frame;
+    rp.window = pl.window;
+    rp.ref_frame = pl.ref_frame;
+    rp.block_k = pl.block_k;
     rp.scale = a.scale;
     rp.limit = a.bound_limit;
     rp.chunks = (pl.n_qblocks + kReduceQB - 1) / kReduceQB;
