@@ -792,11 +792,16 @@ struct AttnKernel {
 
         // stage s but the last: two full sub-steps, each with a next one,
         // the barrier between them, then the loads of stage s + 3 (if it
-        // exists)
+        // exists). The barrier's wait leaves stage s + 2's loads in flight
+        // when that stage exists; when it does not (the last such stage),
+        // stage s + 1's are the newest and the wait must drain them.
         int s = 0;
         auto body = [&](char *bc, char *bn, char *bl) {
             step<NG, ONLINE, false, true>(bc, bc + G::SUB_BYTES, ro, rw, p.c);
-            stage_barrier<LPS>();
+            if (s + 2 < nst)
+                stage_barrier<LPS>();
+            else
+                stage_barrier<0>();
             if (s + 3 < nst) issue_stage(krs, vrs, lo, next_src(crs, tt, sig, e0, nquart, hpb, p.block_k), bl);
             step<NG, ONLINE, false, true>(bc + G::SUB_BYTES, bn, ro, rw, p.c);
             ++s;
