@@ -157,6 +157,9 @@ fsa_status fsa_pre_attention(const void *x, const void *w_qkv, int32_t batch,
     if (heads < 0) return fail(FSA_ERR_INVALID_ARG, "heads = %d, must be >= 0", heads);
     if (channels <= 0 || channels % 32)
         return fail(FSA_ERR_UNSUPPORTED, "channels = %d; must be a positive multiple of 32", channels);
+    // a workgroup's 256 x rows are addressed with 32-bit byte offsets
+    if (channels > kMaxPreChannels)
+        return fail(FSA_ERR_UNSUPPORTED, "channels = %d; at most %d", channels, kMaxPreChannels);
     if (head_dim <= 0) return fail(FSA_ERR_INVALID_ARG, "head_dim = %d, must be > 0", head_dim);
     if (head_dim != 64 && head_dim != 128)
         return fail(FSA_ERR_UNSUPPORTED, "head_dim = %d; built for 64 and 128", head_dim);

@@ -66,5 +66,7 @@ const char *hip_error_text(int code);
 // Largest number of workgroups one launch may use (grid x times 256 threads
 // must stay below 2^32).
 constexpr int64_t kMaxWorkgroups = (int64_t(1) << 32) / 1024 - 1;
+// fsa_pre_attention's largest channel count: 256 rows of x at 32-bit byte offsets.
+constexpr int32_t kMaxPreChannels = 1 << 20;
 
 }  // namespace fsa

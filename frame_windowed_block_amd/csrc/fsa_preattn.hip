@@ -12,9 +12,11 @@
 // Eight wavefronts in a 4 x 2 grid, each owning 64 tokens x 128 features (128
 // fp32 accumulators), two per SIMD.
 // * staging: 64 channels (one 128-byte line per row) per stage, two stages in
-//   LDS, filled by direct global-to-LDS loads issued one stage ahead; rows are
-//   stored with their 16-byte segments XOR-swizzled so that operand reads are
-//   free of bank conflicts;
+//   LDS, filled by direct global-to-LDS buffer loads issued one stage ahead;
+//   rows are stored with their 16-byte segments XOR-swizzled so that operand
+//   reads are free of bank conflicts. Only waves 0-3 issue loads (a quarter of
+//   the next stage after each 16-channel step), so the other wavefront of each
+//   SIMD never waits behind the texture unit and keeps the matrix core busy;
 // * normalisation: each token's sum of squares is accumulated from the x
 //   operand fragments with v_dot2 (bf16 pairs), and 1 / rms scales the fp32
 //   result in the epilogue: diag(r) (x W'^T) = (r x) W'^T;
@@ -55,9 +57,34 @@ struct PreParams {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to bf16 (round to nearest even) in one register, a in the low half.
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    return uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(a))) |
-           (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// Buffer descriptor over `bytes` bytes at `base` (raw, 32-bit data; accesses at
+// or past `bytes` read zeros), in scalar registers.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void *base, int64_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane(uint32_t(b));
+    r[1] = __builtin_amdgcn_readfirstlane(uint32_t(b >> 32) & 0xffffu);
+    r[2] = uint32_t(bytes > int64_t(0xffffffff) ? int64_t(0xffffffff) : bytes);
+    r[3] = 0x00020000u;
+    return r;
+}
+
+// 16 bytes per lane from the buffer at byte offset voff straight into LDS at
+// lds_addr + 16 * lane. Written as an instruction of its own (the asm owns M0)
+// so that the compiler does not wait for it before unrelated LDS reads; the
+// stage barrier waits for it explicitly.
+__device__ __forceinline__ void load_lds16(u32x4 rs, uint32_t lds_addr, int32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(rs)
+                 : "memory", "m0");
 }
 
 // Barrier for a stage hand-off: this wave's direct-to-LDS loads (counted as
@@ -92,29 +119,43 @@ struct PreAttn {
 
     static __device__ __forceinline__ int slot(int row, int seg) { return seg ^ ((row >> 1) & 7); }
 
-    // Direct-to-LDS loads of one stage: each 1 KB load instruction fills 8 rows;
+    // Direct-to-LDS loads of a stage: each 1 KB load instruction fills 8 rows;
     // lane l loads segment slot(row, l % 8) of row l / 8 into slot l % 8, so
-    // every 8 lanes read one whole 128-byte line. Wave w issues the loads of x
-    // rows and of weight rows 64 w .. 64 w + 63. Channels past C (a last stage
-    // that is half empty when C is an odd multiple of 32) read channel 0 and
-    // are zeroed later.
-    static __device__ __forceinline__ void load_stage(const PreParams &p, char *buf, int64_t m0, int32_t f0,
-                                                      int32_t k0) {
+    // every 8 lanes read one whole 128-byte line. Waves 0-3 load everything:
+    // wave w the x and weight rows of row groups w and w + 4 (rows 32 g .. 32 g
+    // + 31 of group g), quarter q of a group being its rows 8 q .. 8 q + 7.
+    // Rows past the last token or projected feature lie past the end of their
+    // buffer and read zeros; a last stage that is half empty (C an odd multiple
+    // of 32) reads the next row's channels there, zeroed in LDS before use.
+    struct Loads {
+        u32x4 xr, wr;               // x rows m0.., weight rows f0..
+        uint32_t lds;               // LDS address of the stage buffers
+        int32_t off[2][4];          // per-lane byte offsets of (group, quarter) in x and w
+    };
+    static __device__ __forceinline__ Loads make_loads(const PreParams &p, const char *smem, int64_t m0, int32_t f0) {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-        const int32_t nf = 3 * p.heads * D;
+        Loads l;
+        l.xr = buffer_rsrc(p.x + m0 * p.channels, (p.tokens - m0) * p.channels * 2);
+        l.wr = buffer_rsrc(p.w + int64_t(f0) * p.channels, int64_t(3 * p.heads * D - f0) * p.channels * 2);
+        l.lds = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((const lds_void *)smem)));
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int row = 32 * wave + 8 * q + lane / 8;
-            const int seg = slot(row, lane % 8);
-            const int32_t kc = k0 + 8 * seg < p.channels ? k0 + 8 * seg : 0;
-            int64_t m = m0 + row;
-            if (m >= p.tokens) m = p.tokens - 1;           // past the end: a valid row, never stored
-            int32_t f = f0 + row;
-            if (f >= nf) f = nf - 1;                        // past the last head part: never stored
-            char *dst = buf + (32 * wave + 8 * q) * ROWB;
-            __builtin_amdgcn_global_load_lds(p.x + m * p.channels + kc, (lds_void *)dst, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(p.w + int64_t(f) * p.channels + kc, (lds_void *)(dst + TM * ROWB),
-                                             16, 0, 0);
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = 32 * ((wave & 3) + 4 * g) + 8 * q + lane / 8;
+                l.off[g][q] = row * p.channels * 2 + slot(row, lane % 8) * 16;
+            }
+        return l;
+    }
+    // Quarter q of both row groups of this wave, channels k0.. of the stage in
+    // LDS buffer `b`.
+    static __device__ __forceinline__ void load_quarter(const Loads &l, int b, int32_t k0, int q) {
+        const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const uint32_t dst = l.lds + uint32_t(b * STAGE) + (32 * ((wave & 3) + 4 * g) + 8 * q) * ROWB;
+            load_lds16(l.xr, dst, l.off[g][q] + 2 * k0);
+            load_lds16(l.wr, dst + TM * ROWB, l.off[g][q] + 2 * k0);
         }
     }
 
@@ -156,17 +197,35 @@ struct PreAttn {
     }
 
     // The four steps of a stage, each step's fragments read while the step
-    // before it is multiplied.
-    static __device__ __forceinline__ void compute(const char *buf, f32x16 (&acc)[4][2], float (&ss)[2]) {
+    // before it is multiplied. With LOAD (waves 0-3 of a stage that has a
+    // successor), the next stage's loads go out a quarter at a time between
+    // the steps.
+    template <bool LOAD>
+    static __device__ __forceinline__ void compute(const char *buf, f32x16 (&acc)[4][2], float (&ss)[2],
+                                                   const Loads &l, int nb, int32_t k0) {
         Frags fa, fb;
         read_frags(buf, 0, fa);
         read_frags(buf, 1, fb);
+        if (LOAD) load_quarter(l, nb, k0, 0);
         step(fa, acc, ss);
         read_frags(buf, 2, fa);
+        if (LOAD) load_quarter(l, nb, k0, 1);
         step(fb, acc, ss);
         read_frags(buf, 3, fb);
+        if (LOAD) load_quarter(l, nb, k0, 2);
         step(fa, acc, ss);
+        if (LOAD) load_quarter(l, nb, k0, 3);
         step(fb, acc, ss);
+    }
+
+    // All stages but the last; LOADER: this wave issues the loads.
+    template <bool LOADER>
+    static __device__ __forceinline__ void main_loop(char *smem, f32x16 (&acc)[4][2], float (&ss)[2], const Loads &l,
+                                                     int stages) {
+        for (int st = 0; st + 1 < stages; ++st) {
+            compute<LOADER>(smem + (st & 1) * STAGE, acc, ss, l, (st + 1) & 1, KC * (st + 1));
+            stage_sync();
+        }
     }
 
     static __device__ void run(const PreParams &p) {
@@ -201,16 +260,21 @@ struct PreAttn {
         // Stage k (64 channels) goes through LDS buffer k % 2; its loads are
         // issued while stage k - 1 is multiplied.
         const int stages = (p.channels + KC - 1) / KC;
-        const bool half_last = (p.channels % KC) != 0;
-        load_stage(p, smem, m0, f0, 0);
+        const Loads l = make_loads(p, smem, m0, f0);
+        const bool loader = __builtin_amdgcn_readfirstlane(wave) < 4;
+        if (loader) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) load_quarter(l, 0, 0, q);
+        }
         stage_sync();
-        for (int st = 0; st < stages; ++st) {
-            if (st + 1 < stages) {
-                load_stage(p, smem + ((st + 1) & 1) * STAGE, m0, f0, KC * (st + 1));
-            } else if (half_last) {
+        if (loader) main_loop<true>(smem, acc, ss, l, stages);
+        else main_loop<false>(smem, acc, ss, l, stages);
+        {
+            const int st = stages - 1;
+            char *buf = smem + (st & 1) * STAGE;
+            if (p.channels % KC != 0) {
                 // channels past C in the last stage: zero them in the x rows so
                 // they add nothing to the products or the squares
-                char *buf = smem + (st & 1) * STAGE;
                 if (t < TM) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -218,7 +282,7 @@ struct PreAttn {
                 }
                 stage_sync();
             }
-            compute(smem + (st & 1) * STAGE, acc, ss);
+            compute<false>(buf, acc, ss, l, 0, 0);
             stage_sync();
         }
 

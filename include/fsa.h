@@ -212,7 +212,8 @@ fsa_status fsa_attention(const fsa_plan_info *plan, const int32_t *d_row_ptr, co
  *          by input channels): q rows of head h at h D, then k, then v.
  * q, k, v: device bf16 [B, H, N, D] outputs; they must not overlap each other
  *          or an input. All five pointers 16-byte aligned.
- * channels C: a positive multiple of 32 (else FSA_ERR_UNSUPPORTED).
+ * channels C: a positive multiple of 32, at most 1,048,576 (else
+ *          FSA_ERR_UNSUPPORTED).
  * head_dim D: 64 or 128 (else FSA_ERR_UNSUPPORTED).
  * eps >= 0 and rope_base > 0, both finite (typical: 1e-6 and 10000).
  * B == 0, N == 0 or H == 0 is a no-op returning FSA_OK. Errors as above.

@@ -162,6 +162,7 @@ def _pre(**kw):
     (dict(heads=-1), fsa.FSA_ERR_INVALID_ARG),
     (dict(channels=48), fsa.FSA_ERR_UNSUPPORTED),
     (dict(channels=0), fsa.FSA_ERR_UNSUPPORTED),
+    (dict(channels=(1 << 20) + 32), fsa.FSA_ERR_UNSUPPORTED),
     (dict(head_dim=96), fsa.FSA_ERR_UNSUPPORTED),
     (dict(head_dim=0), fsa.FSA_ERR_INVALID_ARG),
     (dict(eps=-1.0), fsa.FSA_ERR_INVALID_ARG),
