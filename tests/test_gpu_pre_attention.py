@@ -79,6 +79,11 @@ CASES = [
     ("seq_40_b7", 7, 40, 160, 1, 128),
     ("b2_513_c256", 2, 513, 256, 2, 128),
     ("tile_exact", 1, 512, 64, 2, 64),
+    # several MB of weights: 11 feature tiles (the last one partly past the
+    # last head part) over 3 token tiles; D = 64 with 8 feature tiles and
+    # ragged token tiles crossing a sequence end
+    ("w11_c1024", 1, 600, 1024, 7, 128),
+    ("w8_d64_c1024", 2, 700, 1024, 10, 64),
 ]
 
 
