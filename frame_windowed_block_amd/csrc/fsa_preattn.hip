@@ -162,7 +162,7 @@ struct PreAttn {
     struct Frags { bf16x8 w[4], x[2]; };
 
     // Operand fragments of one 16-channel step: weight rows 128 pp + 32 ot + n
-    // and x rows 128 th + 32 tt + n, channels 16 ks + 8 h .. + 7.
+    // and x rows 64 th + 32 tt + n, channels 16 ks + 8 h .. + 7.
     static __device__ __forceinline__ void read_frags(const char *buf, int ks, Frags &f) {
         const int lane = threadIdx.x & 63, n = lane & 31, h = lane >> 5, wave = threadIdx.x >> 6;
         const int th = wave & 3, pp = wave >> 2;
@@ -175,7 +175,7 @@ struct PreAttn {
             f.x[tt] = *reinterpret_cast<const bf16x8 *>(buf + (64 * th + 32 * tt + n) * ROWB + so);
     }
 
-    // One 16-channel step: 4 x 4 MFMA tiles of 32 x 32 and the squares of the
+    // One 16-channel step: 4 x 2 MFMA tiles of 32 x 32 and the squares of the
     // tokens' channels (used from the pp = 0 waves).
     static __device__ __forceinline__ void step(const Frags &f, f32x16 (&acc)[4][2], float (&ss)[2]) {
 #pragma unroll
