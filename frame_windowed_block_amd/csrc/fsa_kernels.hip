@@ -506,14 +506,14 @@ struct AttnKernel {
     using G = Geo<D>;
     static constexpr int NW = 8;
     static constexpr int THREADS = 64 * NW;
-    static constexpr int KL = 64 * G::SEGS / THREADS;   // 1 KB K (and V) load instructions per wave and stage
-    static constexpr int LPS = 2 * KL;                  // load instructions per wave and stage
+    static constexpr int KL = 64 * G::SEGS / THREADS;   // half the 1 KB K (and V) load instructions of a 16-key tile
+    static constexpr int LPS = 4 * KL;                  // load instructions per loading wave and stage
     static constexpr int RPI = 64 / G::SEGS;            // V rows per load instruction
     static constexpr int NBUF = 4;
     static constexpr int TAB_BYTES = 512;               // per wavefront: two 64-entry tile tables
     static constexpr int LDS_BYTES = NBUF * G::STAGE + NW * TAB_BYTES;
     static_assert(KL >= 1 && NW * KL * 64 == 64 * G::SEGS, "loads cover the stage");
-    static_assert(2 * KL * RPI == 16, "two wavefronts load one 16-key tile");
+    static_assert(2 * KL * RPI == 16, "2 KL instructions cover one 16-key tile");
 
     // The row's 16-key tiles as a table in one vector register: lane l of
     // `cur` holds the byte offset of tile 64 m + l of the row's key list, so
@@ -552,8 +552,8 @@ struct AttnKernel {
     }
     static __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-    // Byte offset of this wavefront's tile (tile wave / 2 of the stage) in
-    // stage `sig` (wave-uniform, counted from 0); advances sig.
+    // Byte offset of this wavefront's tile (tile `wave` of the stage; waves
+    // 0-3 only) in stage `sig` (wave-uniform, counted from 0); advances sig.
     static __device__ __forceinline__ int32_t next_src(u32x4 crs, TileTab &tt, int32_t &sig, int32_t e0,
                                                        int32_t nquart, int hpb, int bk) {
         if ((sig & 15) == 0 && sig > 0) {
@@ -562,14 +562,16 @@ struct AttnKernel {
             tt.cur = (c * bk + 16 * tt.j) * (D * 2);
             tab_issue(crs, e0, nquart, hpb, m + 1, tt);
         }
-        const int i = 4 * (sig & 15) + wave_id() / 2;
+        const int i = 4 * (sig & 15) + wave_id();
         ++sig;
         return __builtin_amdgcn_readlane(tt.cur, i);
     }
 
-    // Direct global -> LDS loads of one stage: wavefronts 2t and 2t + 1 load
-    // 16-key tile t (K and V; the tile's offset `src` is the scalar offset of
-    // the buffer loads), instructions X = KL (w % 2) + x of the tile's 2 KL.
+    // Direct global -> LDS loads of one stage: wavefront t (0-3, one per
+    // SIMD) loads 16-key tile t (K and V; the tile's offset `src` is the
+    // scalar offset of the buffer loads), instructions X = 0 .. 2 KL - 1 of
+    // each. Waves 4-7 issue no loads, so the second wavefront of every SIMD
+    // never stops behind the texture unit and keeps the matrix core fed.
     // K instruction X: lane l loads key l % 16, segment 4 X + l / 16, which
     // is slot 64 X + l of the tile's segment-major layout. V instruction X:
     // lane l loads row RPI X + l / SEGS of the tile into slot l % SEGS, i.e.
@@ -588,14 +590,13 @@ struct AttnKernel {
     }
     static __device__ __forceinline__ void issue_stage(u32x4 krs, u32x4 vrs, const LoadOffsets &lo, int32_t src,
                                                        char *stage) {
-        const int w = wave_id(), t = w / 2;
+        const int t = wave_id();
         char *kt = stage + (t / 2) * G::SUB_BYTES + (t % 2) * G::TILE_K;
         char *vt = stage + (t / 2) * G::SUB_BYTES + G::SUB_K + 16 * (t % 2) * G::ROWB;
-        const int x0 = KL * (w % 2);
 #pragma unroll
-        for (int x = 0; x < KL; ++x) {
-            load_lds16(krs, kt + 1024 * (x0 + x), lo.k, src + 64 * (x0 + x));
-            load_lds16(vrs, vt + 1024 * (x0 + x), lo.v, src + RPI * (x0 + x) * G::ROWB);
+        for (int x = 0; x < 2 * KL; ++x) {
+            load_lds16(krs, kt + 1024 * x, lo.k, src + 64 * x);
+            load_lds16(vrs, vt + 1024 * x, lo.v, src + RPI * x * G::ROWB);
         }
     }
 
@@ -752,11 +753,12 @@ struct AttnKernel {
     // straight into LDS three stages ahead. Stage s sits in buffer s % 4.
     // Its sub-steps 2s and 2s + 1 read K of 2s + 1 and 2s + 2 (the latter in
     // stage s + 1) and V of their own. The barrier after sub-step 2s first
-    // waits for this wavefront's loads of stage s + 1 (only those of stage
-    // s + 2 may still be in flight), so it publishes stage s + 1; every
-    // wavefront has then also finished stage s - 1, whose buffer receives
-    // stage s + 3. NG = 0: a wavefront without rows still loads its share
-    // of every stage and meets every barrier.
+    // waits for this wavefront's loads of stage s + 1 (waves 0-3 load; only
+    // their loads of stage s + 2 may still be in flight), so it publishes
+    // stage s + 1; every wavefront has then also finished stage s - 1, whose
+    // buffer receives stage s + 3. NG = 0: a wavefront without rows still
+    // loads its tile of every stage (if it is one of waves 0-3) and meets
+    // every barrier.
     template <int NG, bool ONLINE>
     static __device__ __forceinline__ void walk(const AttnParams &p, char *smem, const uint16_t *kh,
                                                 const uint16_t *vh, int32_t e0, int32_t nquart, Rows &rw) {
@@ -770,16 +772,17 @@ struct AttnKernel {
         const LoadOffsets lo = load_offsets();
         const ReadOffsets ro = read_offsets();
         TileTab tt;
-        tab_init(col, crs, e0, nquart, hpb, p.block_k, smem + NBUF * G::STAGE + wave_id() * TAB_BYTES, tt);
+        const bool loader = wave_id() < 4;
+        if (loader) tab_init(col, crs, e0, nquart, hpb, p.block_k, smem + NBUF * G::STAGE + wave_id() * TAB_BYTES, tt);
         int32_t sig = 0;
         char *const b0 = smem, *const b1 = smem + G::STAGE, *const b2 = smem + 2 * G::STAGE,
                     *const b3 = smem + 3 * G::STAGE;
 
         // stages 0 .. 2 (those that exist) in flight, 0 and 1 complete
-        issue_stage(krs, vrs, lo, next_src(crs, tt, sig, e0, nquart, hpb, p.block_k), b0);
-        if (nst > 1) issue_stage(krs, vrs, lo, next_src(crs, tt, sig, e0, nquart, hpb, p.block_k), b1);
+        if (loader) issue_stage(krs, vrs, lo, next_src(crs, tt, sig, e0, nquart, hpb, p.block_k), b0);
+        if (loader && nst > 1) issue_stage(krs, vrs, lo, next_src(crs, tt, sig, e0, nquart, hpb, p.block_k), b1);
         if (nst > 2) {
-            issue_stage(krs, vrs, lo, next_src(crs, tt, sig, e0, nquart, hpb, p.block_k), b2);
+            if (loader) issue_stage(krs, vrs, lo, next_src(crs, tt, sig, e0, nquart, hpb, p.block_k), b2);
             stage_barrier<LPS>();
         } else {
             stage_barrier<0>();
@@ -802,7 +805,7 @@ struct AttnKernel {
                 stage_barrier<LPS>();
             else
                 stage_barrier<0>();
-            if (s + 3 < nst) issue_stage(krs, vrs, lo, next_src(crs, tt, sig, e0, nquart, hpb, p.block_k), bl);
+            if (loader && s + 3 < nst) issue_stage(krs, vrs, lo, next_src(crs, tt, sig, e0, nquart, hpb, p.block_k), bl);
             step<NG, ONLINE, false, true>(bc + G::SUB_BYTES, bn, ro, rw, p.c);
             ++s;
         };
@@ -837,7 +840,7 @@ struct AttnKernel {
     }
 
     // This wavefront's tile: rows row0 .. row0 + nvalid - 1 (nvalid 16 or 32)
-    // for NG = 1; NG = 0 stages K/V with the others and meets every barrier.
+    // for NG = 1; NG = 0 meets every barrier (and loads, if one of waves 0-3).
     // CENTRED: the bounds were taken over centred keys; mu is the head's key mean.
     template <int NG, bool CENTRED>
     static __device__ __forceinline__ void tile(const AttnParams &p, char *smem, int64_t head_row0, int32_t row0,
