@@ -14,8 +14,8 @@
 // * staging: 64 channels (one 128-byte line per row) per stage, two stages in
 //   LDS, filled by direct global-to-LDS buffer loads issued one stage ahead;
 //   rows are stored with their 16-byte segments XOR-swizzled so that operand
-//   reads are free of bank conflicts. Only waves 0-3 issue loads (a quarter of
-//   the next stage after each 16-channel step), so the other wavefront of each
+//   reads are free of bank conflicts. Only waves 0-3 issue loads (all of the
+//   next stage's at the start of a stage), so the other wavefront of each
 //   SIMD never waits behind the texture unit and keeps the matrix core busy;
 // * normalisation: each token's sum of squares is accumulated from the x
 //   operand fragments with v_dot2 (bf16 pairs), and 1 / rms scales the fp32
@@ -198,23 +198,23 @@ struct PreAttn {
 
     // The four steps of a stage, each step's fragments read while the step
     // before it is multiplied. With LOAD (waves 0-3 of a stage that has a
-    // successor), the next stage's loads go out a quarter at a time between
-    // the steps.
+    // successor), all of the next stage's loads go out first, so they have
+    // the whole stage to land.
     template <bool LOAD>
     static __device__ __forceinline__ void compute(const char *buf, f32x16 (&acc)[4][2], float (&ss)[2],
                                                    const Loads &l, int nb, int32_t k0) {
         Frags fa, fb;
         read_frags(buf, 0, fa);
         read_frags(buf, 1, fb);
-        if (LOAD) load_quarter(l, nb, k0, 0);
+        if (LOAD) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) load_quarter(l, nb, k0, q);
+        }
         step(fa, acc, ss);
         read_frags(buf, 2, fa);
-        if (LOAD) load_quarter(l, nb, k0, 1);
         step(fb, acc, ss);
         read_frags(buf, 3, fb);
-        if (LOAD) load_quarter(l, nb, k0, 2);
         step(fa, acc, ss);
-        if (LOAD) load_quarter(l, nb, k0, 3);
         step(fb, acc, ss);
     }
 
