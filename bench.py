@@ -28,6 +28,11 @@ between two device synchronisations. Prints ONE JSON line:
 * roofline.traffic: HBM bytes per launch from the committed rocprofv3
   FETCH_SIZE / WRITE_SIZE passes (profiles/traffic.json), reported only while
   the kernel source still matches the one those counters were taken on.
+* two_streams: after the timed steps, 100 steps (after 20 untimed ones) with
+  consecutive steps on two streams in turn (own bounds and output buffers per
+  stream), timed as a whole: a step's kernels then start on the CUs the
+  previous step's attention kernel leaves idle during its last workgroups.
+  value, roofline and check come from the sequential steps only.
 
 --kernel pre_attention times fsa_pre_attention alone (workload pre720 unless
 another pre-attention workload is named) and prints its own JSON line;
@@ -59,6 +64,10 @@ METRIC = "effective TFLOP/s on active blocks + % of bf16 MFMA peak, 25k-token SR
 BOUNDS_EVERY = 4
 # after the timed steps, this many bounds calls run back to back on their own
 BOUNDS_ALONE = 60
+# the two-stream pass: a fixed count of its own (the overlap needs a few steps
+# in flight before it reaches its steady state)
+TWO_STREAM_STEPS = 100
+TWO_STREAM_WARMUP = 20
 PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "frame_windowed_block_amd", "csrc", "fsa_kernels.hip")
@@ -480,13 +489,16 @@ def main():
     bm = torch.empty((bsz, heads), dtype=torch.float32, device=dev)
     mu = torch.empty((bsz, heads, d), dtype=torch.float32, device=dev) if args.center else None
     stream = torch.cuda.current_stream()
+    main_stream, main_bufs = stream, (qn, km, el, bm, o)
     if args.groups > 1 and heads % args.groups:
         print(f"--groups {args.groups} does not divide {heads} heads", file=sys.stderr)
         sys.exit(2)
     group_streams = [torch.cuda.Stream() for _ in range(args.groups)] if args.groups > 1 else []
 
-    def step(i, ev=None):
+    def step(i, ev=None, strm=None, bufs=None):
         q, k, v = inputs[i % len(inputs)]
+        stream = main_stream if strm is None else strm
+        qn, km, el, bm, o = main_bufs if bufs is None else bufs
         slot = i & 1
         if copied[slot] is not None:
             copied[slot].synchronize()                  # pinned buffer free again
@@ -575,6 +587,30 @@ def main():
     torch.cuda.synchronize()
     bounds_alone_ms = b0.elapsed_time(b1) / BOUNDS_ALONE
 
+    # the same steps with consecutive steps on two streams in turn (each with
+    # its own bounds and output buffers): a step's kernels may then start on
+    # the CUs that the previous step's attention kernel leaves idle while its
+    # last workgroups finish. Whole-job throughput only (launches overlap, so
+    # no per-kernel timing); the line's own figures stay sequential.
+    pstreams = [stream, torch.cuda.Stream()]
+    pbufs = [(torch.empty_like(qn), torch.empty_like(km), torch.empty_like(el), torch.empty_like(bm),
+              torch.empty_like(o)) for _ in range(2)]
+    torch.cuda.synchronize()
+    for i in range(TWO_STREAM_WARMUP):
+        step(i, strm=pstreams[i % 2], bufs=pbufs[i % 2])
+    torch.cuda.synchronize()
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
+    pstreams[1].wait_event(p0)
+    for i in range(TWO_STREAM_STEPS):
+        step(i, strm=pstreams[i % 2], bufs=pbufs[i % 2])
+    fin = torch.cuda.Event()
+    fin.record(pstreams[1])
+    stream.wait_event(fin)
+    p1.record(stream)
+    torch.cuda.synchronize()
+    pipe_ms = p0.elapsed_time(p1) / TWO_STREAM_STEPS
+
     flops = plan_flops(info0, bsz, heads, d)
     ms_per_step = total_ms / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -632,6 +668,13 @@ def main():
             "median_ms": round(float(np.median(attn_ms)), 5),
             "p10_ms": round(float(np.percentile(attn_ms, 10)), 5),
             "p90_ms": round(float(np.percentile(attn_ms, 90)), 5),
+        },
+        "two_streams": {
+            "steps": TWO_STREAM_STEPS,
+            "warmup": TWO_STREAM_WARMUP,
+            "ms_per_step": round(pipe_ms, 5),
+            "value": round(flops / (pipe_ms * 1e-3) / 1e12, 3),
+            "note": "the same steps, consecutive steps on two streams in turn",
         },
         "bounds": {
             "kernels": "fsa_bounds (norms + bound reduce)",
