@@ -367,11 +367,14 @@ def bench_chain(args):
     el = torch.empty((pw.batch, pw.heads), dtype=torch.int32, device=dev)
     bm = torch.empty((pw.batch, pw.heads), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    main_bufs = (q, k, v, o, qn, km, el, bm)
 
-    def step(i):
-        fsa.pre_attention(xs[i % len(xs)], wd, pw.heads, pw.head_dim, q=q, k=k, v=v, stream=stream)
-        fsa.bounds(dplan, q, k, aw.scale, 0.0, 0, 0, qn, km, el, bm, stream=stream)
-        fsa.attention(dplan, q, k, v, qn, km, el, aw.scale, 0, 0, out=o, stream=stream)
+    def step(i, strm=None, bufs=None):
+        s_ = stream if strm is None else strm
+        q, k, v, o, qn, km, el, bm = main_bufs if bufs is None else bufs
+        fsa.pre_attention(xs[i % len(xs)], wd, pw.heads, pw.head_dim, q=q, k=k, v=v, stream=s_)
+        fsa.bounds(dplan, q, k, aw.scale, 0.0, 0, 0, qn, km, el, bm, stream=s_)
+        fsa.attention(dplan, q, k, v, qn, km, el, aw.scale, 0, 0, out=o, stream=s_)
 
     preroll_ms, _ = preroll(step, args.preroll_ms)
     for i in range(args.warmup):
@@ -385,6 +388,23 @@ def bench_chain(args):
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
+    # the same steps, consecutive steps on two streams in turn (own buffers)
+    pstreams = [stream, torch.cuda.Stream()]
+    pbufs = [tuple(torch.empty_like(t) for t in main_bufs) for _ in range(2)]
+    for i in range(TWO_STREAM_WARMUP):
+        step(i, pstreams[i % 2], pbufs[i % 2])
+    torch.cuda.synchronize()
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
+    pstreams[1].wait_event(p0)
+    for i in range(TWO_STREAM_STEPS):
+        step(i, pstreams[i % 2], pbufs[i % 2])
+    fin = torch.cuda.Event()
+    fin.record(pstreams[1])
+    stream.wait_event(fin)
+    p1.record(stream)
+    torch.cuda.synchronize()
+    pipe_ms = p0.elapsed_time(p1) / TWO_STREAM_STEPS
     pre_flops = projection_flops(pw.batch, pw.seq_len, pw.channels, pw.heads, pw.head_dim)
     attn_flops = plan_flops(info, pw.batch, pw.heads, pw.head_dim)
     line = {
@@ -398,6 +418,10 @@ def bench_chain(args):
                    "attention_flops": attn_flops, "eligible_heads": int(el.sum().item())},
         "pct_of_peak": round(100.0 * (pre_flops + attn_flops) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "timing": {"preroll_ms": round(preroll_ms, 1)},
+        "two_streams": {"steps": TWO_STREAM_STEPS, "warmup": TWO_STREAM_WARMUP,
+                        "ms_per_step": round(pipe_ms, 5),
+                        "value": round((pre_flops + attn_flops) / (pipe_ms * 1e-3) / 1e12, 3),
+                        "note": "the same steps, consecutive steps on two streams in turn"},
     }
     print(json.dumps(line), flush=True)
 
