@@ -278,9 +278,10 @@ def bench_pre_attention(args):
     outs = [torch.empty(shape, dtype=torch.bfloat16, device=dev) for _ in range(3)]
     stream = torch.cuda.current_stream()
 
-    def step(i):
-        fsa.pre_attention(xs[i % len(xs)], wd, wl.heads, wl.head_dim, q=outs[0], k=outs[1],
-                          v=outs[2], stream=stream)
+    def step(i, strm=None, o3=None):
+        o3 = outs if o3 is None else o3
+        fsa.pre_attention(xs[i % len(xs)], wd, wl.heads, wl.head_dim, q=o3[0], k=o3[1],
+                          v=o3[2], stream=stream if strm is None else strm)
 
     preroll_ms, _ = preroll(step, args.preroll_ms)
     for i in range(args.warmup):
@@ -299,6 +300,23 @@ def bench_pre_attention(args):
     torch.cuda.synchronize()
     ms = np.array([a.elapsed_time(b) for a, b in evs])
     total_ms = t0.elapsed_time(t1)
+    # the same calls, consecutive calls on two streams in turn (own outputs)
+    pstreams = [stream, torch.cuda.Stream()]
+    pouts = [[torch.empty_like(t) for t in outs] for _ in range(2)]
+    for i in range(TWO_STREAM_WARMUP):
+        step(i, pstreams[i % 2], pouts[i % 2])
+    torch.cuda.synchronize()
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
+    pstreams[1].wait_event(p0)
+    for i in range(TWO_STREAM_STEPS):
+        step(i, pstreams[i % 2], pouts[i % 2])
+    fin = torch.cuda.Event()
+    fin.record(pstreams[1])
+    stream.wait_event(fin)
+    p1.record(stream)
+    torch.cuda.synchronize()
+    pipe_ms = p0.elapsed_time(p1) / TWO_STREAM_STEPS
     flops = projection_flops(wl.batch, wl.seq_len, wl.channels, wl.heads, wl.head_dim)
     kbytes = 2 * wl.batch * wl.seq_len * wl.channels + \
         2 * 3 * wl.heads * wl.head_dim * wl.channels + 3 * 2 * wl.batch * wl.heads * wl.seq_len * wl.head_dim
@@ -324,6 +342,10 @@ def bench_pre_attention(args):
         },
     }
     line["timing"] = {"preroll_ms": round(preroll_ms, 1)}
+    line["two_streams"] = {"steps": TWO_STREAM_STEPS, "warmup": TWO_STREAM_WARMUP,
+                           "ms_per_step": round(pipe_ms, 5),
+                           "value": round(flops / (pipe_ms * 1e-3) / 1e12, 3),
+                           "note": "the same calls, consecutive calls on two streams in turn"}
     if not args.no_cpu_baseline:
         import oracle
         line["cpu_baseline"] = cpu_baseline_pre(wl, x, gain, w)
