@@ -18,8 +18,9 @@
 //   next stage's at the start of a stage), so the other wavefront of each
 //   SIMD never waits behind the texture unit and keeps the matrix core busy;
 // * normalisation: each token's sum of squares is accumulated from the x
-//   operand fragments with v_dot2 (bf16 pairs), and 1 / rms scales the fp32
-//   result in the epilogue: diag(r) (x W'^T) = (r x) W'^T;
+//   operand fragments with v_dot2 (bf16 pairs) by waves 4-7 (the waves that
+//   issue no loads), and 1 / rms scales the fp32 result in the epilogue:
+//   diag(r) (x W'^T) = (r x) W'^T;
 // * rotary embedding (q and k): with the features as MFMA rows, features j and
 //   j + D/2 of a token sit in the same lane and register (output tiles ot and
 //   ot + D/64), so the rotation is lane-local. Angles are taken in revolutions
@@ -175,11 +176,12 @@ struct PreAttn {
             f.x[tt] = *reinterpret_cast<const bf16x8 *>(buf + (64 * th + 32 * tt + n) * ROWB + so);
     }
 
-    // One 16-channel step: 4 x 2 MFMA tiles of 32 x 32 and the squares of the
-    // tokens' channels (used from the pp = 0 waves).
+    // One 16-channel step: 4 x 2 MFMA tiles of 32 x 32 and, with SQ (waves
+    // 4-7, which issue no loads), the squares of the tokens' channels.
+    template <bool SQ>
     static __device__ __forceinline__ void step(const Frags &f, f32x16 (&acc)[4][2], float (&ss)[2]) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
+        for (int tt = 0; tt < 2 && SQ; ++tt) {
             const bf16x2 p0 = __builtin_shufflevector(f.x[tt], f.x[tt], 0, 1);
             const bf16x2 p1 = __builtin_shufflevector(f.x[tt], f.x[tt], 2, 3);
             const bf16x2 p2 = __builtin_shufflevector(f.x[tt], f.x[tt], 4, 5);
@@ -200,7 +202,7 @@ struct PreAttn {
     // before it is multiplied. With LOAD (waves 0-3 of a stage that has a
     // successor), all of the next stage's loads go out first, so they have
     // the whole stage to land.
-    template <bool LOAD>
+    template <bool LOAD, bool SQ>
     static __device__ __forceinline__ void compute(const char *buf, f32x16 (&acc)[4][2], float (&ss)[2],
                                                    const Loads &l, int nb, int32_t k0) {
         Frags fa, fb;
@@ -210,22 +212,39 @@ struct PreAttn {
 #pragma unroll
             for (int q = 0; q < 4; ++q) load_quarter(l, nb, k0, q);
         }
-        step(fa, acc, ss);
+        step<SQ>(fa, acc, ss);
         read_frags(buf, 2, fa);
-        step(fb, acc, ss);
+        step<SQ>(fb, acc, ss);
         read_frags(buf, 3, fb);
-        step(fa, acc, ss);
-        step(fb, acc, ss);
+        step<SQ>(fa, acc, ss);
+        step<SQ>(fb, acc, ss);
     }
 
-    // All stages but the last; LOADER: this wave issues the loads.
+    // Every stage; LOADER (waves 0-3): this wave issues the loads, the others
+    // (waves 4-7) take the squares. One instantiation per role, the last
+    // stage included, so that the register allocation of each is one piece.
     template <bool LOADER>
     static __device__ __forceinline__ void main_loop(char *smem, f32x16 (&acc)[4][2], float (&ss)[2], const Loads &l,
-                                                     int stages) {
+                                                     int stages, int channels) {
         for (int st = 0; st + 1 < stages; ++st) {
-            compute<LOADER>(smem + (st & 1) * STAGE, acc, ss, l, (st + 1) & 1, KC * (st + 1));
+            compute<LOADER, !LOADER>(smem + (st & 1) * STAGE, acc, ss, l, (st + 1) & 1, KC * (st + 1));
             stage_sync();
         }
+        const int st = stages - 1;
+        char *buf = smem + (st & 1) * STAGE;
+        if (channels % KC != 0) {
+            // channels past C in the last stage: zero them in the x rows so
+            // they add nothing to the products or the squares
+            const int t = threadIdx.x;
+            if (t < TM) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<u32x4 *>(buf + t * ROWB + slot(t, 4 + i) * 16) = u32x4{};
+            }
+            stage_sync();
+        }
+        compute<false, !LOADER>(buf, acc, ss, l, 0, 0);
+        stage_sync();
     }
 
     static __device__ void run(const PreParams &p) {
@@ -267,28 +286,13 @@ struct PreAttn {
             for (int q = 0; q < 4; ++q) load_quarter(l, 0, 0, q);
         }
         stage_sync();
-        if (loader) main_loop<true>(smem, acc, ss, l, stages);
-        else main_loop<false>(smem, acc, ss, l, stages);
-        {
-            const int st = stages - 1;
-            char *buf = smem + (st & 1) * STAGE;
-            if (p.channels % KC != 0) {
-                // channels past C in the last stage: zero them in the x rows so
-                // they add nothing to the products or the squares
-                if (t < TM) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        *reinterpret_cast<u32x4 *>(buf + t * ROWB + slot(t, 4 + i) * 16) = u32x4{};
-                }
-                stage_sync();
-            }
-            compute<false>(buf, acc, ss, l, 0, 0);
-            stage_sync();
-        }
+        if (loader) main_loop<true>(smem, acc, ss, l, stages, p.channels);
+        else main_loop<false>(smem, acc, ss, l, stages, p.channels);
 
-        // 1 / rms per token, from the pp = 0 waves (the two halves of a wave hold
-        // disjoint channel halves of each token)
-        if (pp == 0) {
+        // 1 / rms per token, from the pp = 1 waves (waves 4-7, which took the
+        // squares; the two halves of a wave hold disjoint channel halves of
+        // each token)
+        if (pp == 1) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const float sq = ss[tt] + __shfl_xor(ss[tt], 32);
