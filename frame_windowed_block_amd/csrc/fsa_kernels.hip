@@ -728,8 +728,17 @@ struct AttnKernel {
             if constexpr (NEXT) read_k(nxt, ro, ka);
             read_v<PVK>(cur, ro, va);
             bf16x8 pk[2];
-            weights<ONLINE, PVK>(rw, c, pk);
-            if constexpr (NEXT) rw.s = qk(ka, rw.qf);
+            if constexpr (ONLINE && NEXT) {
+                // the fallback's rescale branch splits the step in two blocks:
+                // the next scores' MFMAs go first, so they run under the max
+                // and the branch instead of waiting behind them
+                const f32x16 sn = qk(ka, rw.qf);
+                weights<ONLINE, PVK>(rw, c, pk);
+                rw.s = sn;
+            } else {
+                weights<ONLINE, PVK>(rw, c, pk);
+                if constexpr (NEXT) rw.s = qk(ka, rw.qf);
+            }
 #pragma unroll
             for (int ks = 0; ks < PVK; ++ks)
 #pragma unroll
