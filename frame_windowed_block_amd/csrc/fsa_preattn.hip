@@ -116,7 +116,7 @@ struct PreAttn {
     static constexpr int OUT_ROW = 128 * 2 + 16;
     static constexpr int OUT_WAVE = 64 * OUT_ROW;
     static constexpr int MAIN_BYTES = 2 * STAGE > 8 * OUT_WAVE ? 2 * STAGE : 8 * OUT_WAVE;
-    static constexpr int LDS_BYTES = MAIN_BYTES + TM * 4 + (D / 2) * 8;
+    static constexpr int LDS_BYTES = MAIN_BYTES + TM * 4 + (D / 2) * 8 + TM * 8;
 
     static __device__ __forceinline__ int slot(int row, int seg) { return seg ^ ((row >> 1) & 7); }
 
@@ -251,6 +251,7 @@ struct PreAttn {
         __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
         float *rs = reinterpret_cast<float *>(smem + MAIN_BYTES);
         float2 *rot = reinterpret_cast<float2 *>(smem + MAIN_BYTES + TM * 4);
+        int64_t *rowoff = reinterpret_cast<int64_t *>(smem + MAIN_BYTES + TM * 4 + (D / 2) * 8);
 
         const int64_t bid = blockIdx.x;
         const int64_t L = (bid & 7) * p.per_xcd + (bid >> 3);
@@ -270,6 +271,16 @@ struct PreAttn {
             const double f = exp2(-(2.0 * t / D) * log2(double(p.rope_base))) * (0.5 / M_PI);
             const double u = double(pos0) * f;
             rot[t] = make_float2(float(f), float(u - floor(u)));
+        }
+        // Output token of each tile row, b N H + n for sequence b and position n
+        // (the tile may cross sequence ends), -1 past the last token: one
+        // division per row here instead of one per row and store later.
+        if (t < TM) {
+            const uint32_t pf = uint32_t(pos0) + uint32_t(t);
+            const uint32_t wraps = pf / uint32_t(p.seq_len);
+            rowoff[t] = m0 + t < p.tokens
+                            ? (b0 + wraps) * p.heads * int64_t(p.seq_len) + (pf - wraps * uint32_t(p.seq_len))
+                            : int64_t(-1);
         }
 
         f32x16 acc[4][2];
@@ -367,6 +378,7 @@ struct PreAttn {
         const int32_t nparts = 3 * p.heads;
         constexpr int LPR = D / 8;                          // lanes per token row of one head part
         constexpr int RPI = 64 / LPR;                       // token rows per store instruction
+        constexpr int NJ = 64 / RPI;                        // store instructions per head part
 #pragma unroll
         for (int part_i = 0; part_i < 128 / D; ++part_i) {
             const int32_t fbase = f0 + 128 * pp + D * part_i;
@@ -374,17 +386,26 @@ struct PreAttn {
             if (part >= nparts) continue;
             const int qkv = part / p.heads, head = part % p.heads;
             uint16_t *out = (qkv == 0 ? p.q : (qkv == 1 ? p.k : p.v)) + int64_t(head) * p.seq_len * D;
-#pragma unroll 4
-            for (int r0 = 0; r0 < 64; r0 += RPI) {
-                const int rw = r0 + lane / LPR;              // the wave's token row
-                const int row = 64 * th + rw;                // the workgroup's token row
-                if (m0 + row >= p.tokens) continue;
-                const uint32_t pf = uint32_t(pos0) + uint32_t(row);
-                const uint32_t wraps = pf / uint32_t(p.seq_len);
-                const int64_t tok = ((b0 + wraps) * p.heads * int64_t(p.seq_len) + (pf - wraps * uint32_t(p.seq_len))) * D;
-                const u32x4 v = *reinterpret_cast<const u32x4 *>(park + rw * OUT_ROW + (D * part_i + 8 * (lane % LPR)) * 2);
-                // streaming store: the outputs are not read again by this kernel
-                __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(out + tok + 8 * (lane % LPR)));
+            // all of the part's LDS reads first, then the stores (one wait)
+            u32x4 v[NJ];
+            int64_t tok[NJ];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int rw = RPI * j + lane / LPR;         // the wave's token row
+                tok[j] = rowoff[64 * th + rw];
+                v[j] = *reinterpret_cast<const u32x4 *>(park + rw * OUT_ROW + (D * part_i + 8 * (lane % LPR)) * 2);
+            }
+            // streaming stores: the outputs are not read again by this kernel;
+            // only the last token tile has rows past the end
+            if (m0 + TM <= p.tokens) {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    __builtin_nontemporal_store(v[j], reinterpret_cast<u32x4 *>(out + tok[j] * D + 8 * (lane % LPR)));
+            } else {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    if (tok[j] >= 0)
+                        __builtin_nontemporal_store(v[j], reinterpret_cast<u32x4 *>(out + tok[j] * D + 8 * (lane % LPR)));
             }
         }
     }
