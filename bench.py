@@ -127,33 +127,82 @@ def projection_flops(batch: int, seq_len: int, channels: int, heads: int, head_d
     return 2 * batch * seq_len * channels * 3 * heads * head_dim
 
 
+def parse_dpm_mhz(line: str):
+    """MHz of one ``pp_dpm_sclk`` line ("1: 1989Mhz *"), or None."""
+    import re
+    m = re.search(r"(\d+(?:\.\d+)?)\s*[Mm][Hh]z", line)
+    return float(m.group(1)) if m else None
+
+
 class ClockSampler:
-    """Engine clock (sclk, MHz) of GPU 0, sampled by a background thread through
-    amdsmi while a region runs. Any failure (no amdsmi, no permission) leaves
-    the samples empty and records why; the run itself is unaffected."""
+    """Engine clock (sclk, MHz) of GPU 0, sampled by a background thread while a
+    region runs. The source is the driver's sysfs ``pp_dpm_sclk`` (the level
+    marked current), which follows the clock within a fraction of a second;
+    amdsmi's clock query is the fallback, but its value is refreshed only about
+    once a second, so over a short region it can still show an earlier (even
+    idle) clock. Any failure leaves the samples empty and records why; the run
+    itself is unaffected."""
 
     def __init__(self, period_s: float = 0.004):
         self.period = period_s
         self.samples: list[float] = []
         self.error = None
+        self.source = None
         self._stop = None
         self._thread = None
         self._smi = None
         self._handle = None
+        self._sysfs = None
         try:
             import amdsmi
             amdsmi.amdsmi_init()
             self._smi = amdsmi
             self._handle = amdsmi.amdsmi_get_processor_handles()[0]
-            self.read()
         except Exception as exc:                       # noqa: BLE001
             self.error = f"{type(exc).__name__}: {exc}"
             self._smi = None
+        self._sysfs = self._find_sysfs()
+        try:
+            if self._sysfs is not None and self._read_sysfs() is not None:
+                self.source = "sysfs pp_dpm_sclk"
+            elif self._smi is not None and self._read_smi() is not None:
+                self.source = "amdsmi clock info (refreshed about once a second)"
+        except Exception as exc:                       # noqa: BLE001
+            self.error = f"{type(exc).__name__}: {exc}"
 
-    def read(self):
+    def _find_sysfs(self):
+        import glob
+        paths = []
+        if self._smi is not None:
+            try:
+                bdf = self._smi.amdsmi_get_gpu_device_bdf(self._handle)
+                paths.append(f"/sys/bus/pci/devices/{bdf}/pp_dpm_sclk")
+            except Exception:                          # noqa: BLE001
+                pass
+        cards = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        if len(cards) == 1:                            # the only GPU: no need to match it
+            paths.append(cards[0])
+        for path in paths:
+            if os.path.exists(path):
+                return path
+        return None
+
+    def _read_sysfs(self):
+        with open(self._sysfs) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):        # e.g. "1: 1989Mhz *"
+                    return parse_dpm_mhz(line)
+        return None
+
+    def _read_smi(self):
         info = self._smi.amdsmi_get_clock_info(self._handle, self._smi.AmdSmiClkType.GFX)
         clk = info.get("clk")
         return float(clk) if isinstance(clk, (int, float)) else None
+
+    def read(self):
+        if self.source is None:
+            return None
+        return self._read_sysfs() if self.source.startswith("sysfs") else self._read_smi()
 
     def _loop(self):
         while not self._stop.is_set():
@@ -181,9 +230,10 @@ class ClockSampler:
             self._thread.join()
             self._thread = None
         if not self.samples:
-            return {"samples": 0, "error": self.error or "no samples"}
+            return {"samples": 0, "error": self.error or "no samples", "source": self.source}
         x = sorted(self.samples)
-        return {"samples": len(x), "mean": round(sum(x) / len(x), 1), "min": x[0], "max": x[-1]}
+        return {"samples": len(x), "mean": round(sum(x) / len(x), 1), "min": x[0], "max": x[-1],
+                "source": self.source}
 
 
 def parse():

@@ -47,6 +47,15 @@ def test_traffic_is_reported_only_for_the_profiled_kernel_source(tmp_path):
     assert bench.measured_traffic("fsa_attention", "no_such_workload") is None
 
 
+def test_dpm_clock_line_parsing():
+    """The sampler reads the current level of the driver's pp_dpm_sclk table."""
+    import bench
+    assert bench.parse_dpm_mhz("1: 1989Mhz *") == 1989.0
+    assert bench.parse_dpm_mhz("S: 95Mhz *") == 95.0
+    assert bench.parse_dpm_mhz("0: 500Mhz") == 500.0
+    assert bench.parse_dpm_mhz("no clock here") is None
+
+
 def test_output_check_bars():
     """The bench line's check: every element within the oracle's element bar
     (1e-2, raised to half a bf16 spacing plus the arithmetic's error only where
