@@ -112,7 +112,7 @@ struct PreAttn {
     // so an operand read of 16 consecutive rows covers all 64 banks once.
     static constexpr int ROWB = KC * 2;
     static constexpr int STAGE = (TM + TN) * ROWB;
-    // write-out: per wave 128 token rows of 128 bf16 features, 16-byte pad per row
+    // write-out: per wave 64 token rows of 128 bf16 features, 16-byte pad per row
     static constexpr int OUT_ROW = 128 * 2 + 16;
     static constexpr int OUT_WAVE = 64 * OUT_ROW;
     static constexpr int MAIN_BYTES = 2 * STAGE > 8 * OUT_WAVE ? 2 * STAGE : 8 * OUT_WAVE;
@@ -357,7 +357,7 @@ struct PreAttn {
             }
         }
 
-        // Write-out through LDS: each wave parks its 128 tokens x 128 features as
+        // Write-out through LDS: each wave parks its 64 tokens x 128 features as
         // bf16 rows of 256 B (plus a 16-byte pad) in the free stage buffers,
         // then stores whole token rows of each head part with 16-byte lanes.
         stage_sync();                                       // every wave is done with the stage buffers
