@@ -103,7 +103,12 @@ fsa_status fsa_bounds(const fsa_plan_info *plan, const int32_t *d_row_ptr, const
     if (units / 4 + 1 > kMaxWorkgroups || int64_t(batch) * hc * plan->n_qblocks > kMaxWorkgroups)
         return fail(FSA_ERR_UNSUPPORTED, "problem needs more workgroups than one launch holds");
     if (!(bound_limit > 0.0f)) bound_limit = 32.0f;               // <= 0 or NaN: default
-    BoundsLaunch a{plan, d_row_ptr, d_col_idx, q, k, batch, heads, head_dim, head_offset, hc,
+    // Any window of at least F frames gives the same (dense) mask; the
+    // kernels get it clamped to F so that their window-edge arithmetic
+    // (frame + window, in 32 bits) cannot overflow.
+    fsa_plan_info pl = *plan;
+    if (pl.window > pl.frames) pl.window = pl.frames;
+    BoundsLaunch a{&pl, d_row_ptr, d_col_idx, q, k, batch, heads, head_dim, head_offset, hc,
                    scale, bound_limit, qnorm, kmax, eligible, bmax, kmean, stream};
     const int err = launch_bounds(a);
     if (err) return fail(FSA_ERR_HIP, "fsa_bounds launch failed: %s", hip_error_text(err));

@@ -86,6 +86,7 @@ SMALL = [
     ("t1200_small", 1, 1, 128, 3, 1200, 1, 0, 240, 80),
     ("t144_d64_b2", 2, 2, 64, 4, 144, 1, 2, 144, 48),
     ("t32_dense", 1, 2, 128, 6, 32, 9, 0, 32, 32),
+    ("wmax_dense", 1, 2, 128, 4, 48, 2**31 - 1, 1, 48, 16),    # largest window: dense mask
     # rows whose 16-key tile counts sit at the edges of the walk's 64-tile
     # offset tables: 64 and 128 tiles (frames 0 and 1), 65, 126 (D = 64,
     # three tiles per block) and 129 (one tile per block, a 688-row query

@@ -101,3 +101,14 @@ def test_large_window_and_single_frame():
     _same(3, 16, 2**30, 2)
     info = _same(14, 1200, 13, 0)
     assert info.nnz == info.n_qblocks * info.n_kblocks
+
+
+@pytest.mark.parametrize("r", [0, 2, 3])
+def test_largest_window_is_dense(r):
+    """w = 2^31 - 1 (no overflow in the frame arithmetic) lists every key block
+    of every row, the same plan as w = F - 1."""
+    info = _same(4, 48, 2**31 - 1, r, 48, 16)
+    dense, drow, dcol = fsa.plan(4, 48, 3, r, 48, 16)
+    _, row_ptr, col_idx = fsa.plan(4, 48, 2**31 - 1, r, 48, 16)
+    assert info.nnz == info.n_qblocks * info.n_kblocks == dense.nnz
+    assert row_ptr.tobytes() == drow.tobytes() and col_idx.tobytes() == dcol.tobytes()
