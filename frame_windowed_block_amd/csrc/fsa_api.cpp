@@ -145,6 +145,10 @@ fsa_status fsa_attention(const fsa_plan_info *plan, const int32_t *d_row_ptr, co
     }
     if (int64_t(batch) * hc * plan->n_qblocks + 8 > kMaxWorkgroups)
         return fail(FSA_ERR_UNSUPPORTED, "problem needs more workgroups than one launch holds");
+    // the kernel reads the block list with 32-bit byte offsets from its start
+    if (int64_t(plan->nnz) * 4 >= (int64_t(1) << 31))
+        return fail(FSA_ERR_UNSUPPORTED, "plan has %d active blocks; the block list must stay below 2 GiB "
+                    "(at most 2^29 - 1 blocks)", plan->nnz);
     AttentionLaunch a{plan, d_row_ptr, d_col_idx, q, k, v, o, qnorm, kmax, eligible, kmean,
                       batch, heads, head_dim, head_offset, hc, scale, stream};
     const int err = launch_attention(a);

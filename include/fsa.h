@@ -163,7 +163,8 @@ fsa_status fsa_bounds(const fsa_plan_info *plan, const int32_t *d_row_ptr, const
  * p is rounded to bf16 for the p.v product; o is rounded to bf16 (RNE).
  *
  * plan, d_row_ptr, d_col_idx: as for fsa_bounds (the CSR must be the one
- *             fsa_plan produced for `plan`).
+ *             fsa_plan produced for `plan`). The block list (nnz * 4 bytes)
+ *             must be below 2 GiB, i.e. nnz < 2^29 (else FSA_ERR_UNSUPPORTED).
  * q, k, v:    device bf16 [B, H, N, D] inputs; o: device bf16 [B, H, N, D]
  *             output; all 16-byte aligned; o must not overlap the inputs.
  * qnorm, kmax, eligible, kmean: the outputs of fsa_bounds for the same q, k,

@@ -197,3 +197,13 @@ def test_head_slab_limit():
     assert st == fsa.FSA_ERR_UNSUPPORTED and "2 GiB" in msg
     st, msg = _attn(info, head_dim=128)
     assert st == fsa.FSA_ERR_UNSUPPORTED and "2 GiB" in msg
+
+
+def test_block_list_limit():
+    """fsa_attention reads the plan's block list with 32-bit byte offsets:
+    nnz * 4 must stay below 2 GiB (rejected before anything is launched)."""
+    f = 23171                                   # dense: f^2 = 536,895,241 >= 2^29 blocks
+    info = _abi.PlanInfo(frames=f, tokens_per_frame=16, window=f - 1, ref_frame=0, seq_len=16 * f,
+                         block_q=16, block_k=16, n_qblocks=f, n_kblocks=f, nnz=f * f)
+    st, msg = _attn(info, head_dim=128)
+    assert st == fsa.FSA_ERR_UNSUPPORTED and "block list" in msg
