@@ -60,8 +60,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "effective TFLOP/s on active blocks + % of bf16 MFMA peak, 25k-token SR attn"
-# fsa_bounds is bracketed by timing events on every BOUNDS_EVERY-th timed step
-BOUNDS_EVERY = 4
+# fsa_bounds and fsa_attention are bracketed by timing events on every
+# EVENTS_EVERY-th timed step only: an event recorded between two kernels holds
+# the stream for a few microseconds, so the other steps record just the plan
+# buffer's reuse marker after the attention kernel
+EVENTS_EVERY = 4
 # after the timed steps, this many bounds calls run back to back on their own
 BOUNDS_ALONE = 60
 # the two-stream pass: a fixed count of its own (the overlap needs a few steps
@@ -613,10 +616,11 @@ def main():
             e.record(copy_stream)
         copied[slot] = e
         stream.wait_event(e)
-        if ev is not None and i % BOUNDS_EVERY == 0:
+        timed = ev is not None and i % EVENTS_EVERY == 0
+        if timed:
             ev[0].record(stream)
         fsa.bounds(dplan, q, k, wl.scale, 0.0, 0, 0, qn, km, el, bm, stream=stream, kmean=mu)
-        if ev is not None:
+        if timed:
             ev[1].record(stream)
         if args.groups <= 1:
             fsa.attention(dplan, q, k, v, qn, km, el, wl.scale, 0, 0, out=o, stream=stream, kmean=mu)
@@ -634,7 +638,7 @@ def main():
                 done = torch.cuda.Event()
                 done.record(gs)
                 stream.wait_event(done)
-        if ev is not None:
+        if timed:
             ev[2].record(stream)
             used[slot] = ev[2]
         else:
@@ -667,8 +671,9 @@ def main():
     torch.cuda.synchronize()
     clk_timed = clocks.stop()
     total_ms = t_start.elapsed_time(t_end)
-    attn_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    bnd_ms = np.array([e[0].elapsed_time(e[1]) for i, e in enumerate(evs) if i % BOUNDS_EVERY == 0])
+    sampled = [e for i, e in enumerate(evs) if i % EVENTS_EVERY == 0]
+    attn_ms = np.array([e[1].elapsed_time(e[2]) for e in sampled])
+    bnd_ms = np.array([e[0].elapsed_time(e[1]) for e in sampled])
 
     # the bounds pass on its own, after the timed steps: BOUNDS_ALONE calls
     # back to back over the rotating input copies, one event pair around them
@@ -760,6 +765,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic("fsa_attention", traffic_key) if args.groups <= 1 else None,
+            "timed_steps": int(attn_ms.size),
             "mean_ms": round(attn_mean, 5),
             "median_ms": round(float(np.median(attn_ms)), 5),
             "p10_ms": round(float(np.percentile(attn_ms, 10)), 5),
