@@ -116,6 +116,16 @@ def make_inputs(wl: Workload, device: str = "cpu"):
     return tuple(out)
 
 
+def make_device_normal(shape, seed: int, device: str):
+    """q, k, v as bf16 N(0, 1) tensors of ``shape``, drawn on ``device`` by one
+    ``torch.Generator(device)`` seeded with ``seed`` (q, k, v in that order),
+    for shapes too large to draw on the host. Deterministic for a given device
+    type and seed; the tests hand the oracle host copies of the slices it needs."""
+    g = torch.Generator(device).manual_seed(seed)
+    return tuple(torch.randn(shape, generator=g, dtype=torch.float32, device=device).to(torch.bfloat16)
+                 for _ in range(3))
+
+
 # Inputs of the fused pre-attention chain (article section "Bố cục là ABI"):
 # token activations x [B, N, C], a per-channel norm gain and the q/k/v
 # projection weight [3 H D, C]. The article gives no model width; C = H D.

@@ -361,3 +361,54 @@ def test_empty_batch_is_noop():
     o, _ = fsa.forward(dplan, q, q.clone(), q.clone(), wl.scale)
     torch.cuda.synchronize()
     assert o.shape == q.shape
+
+
+# ----------------------------------------------------------------- the largest accepted head
+def _frame_reference(q, k, v, f, t, scale):
+    """Oracle output (and bar inputs) of frame f's rows when every frame sees
+    only itself and reference frame 0 (window 0): the attention of a one- or
+    two-frame problem made of frame 0 and frame f."""
+    sl = [slice(0, t)] if f == 0 else [slice(0, t), slice(f * t, (f + 1) * t)]
+    sub = [torch.cat([x[:, :, s] for s in sl], dim=2).cpu() for x in (q, k, v)]
+    wl = synthetic.Workload("frame_sub", 1, 1, q.shape[-1], len(sl), t, 0, 0)
+    assert wl.scale == scale
+    ref = parity.reference(wl, *sub)
+    rows = slice(0, t) if f == 0 else slice(t, 2 * t)
+    return {"o": ref["o"][:, :, rows], "m2": ref["m2"][:, :, rows], "score_bound": ref["score_bound"][:, :, rows],
+            "n_keys": ref["n_keys"][:, :, rows], "head_dim": ref["head_dim"]}
+
+
+def test_largest_head_slab():
+    """The largest head the boundary accepts: N * D * 2 just below 2 GiB (N =
+    8,388,592 tokens at D = 128 in 16-token frames, window 0, reference frame
+    0), so the kernels' 32-bit byte offsets inside the head reach their top.
+    Sampled frames (the first, the last and a spread between) on the bound path
+    and on the forced fallback, against the oracle on the frames each row sees;
+    norms of the same rows and key blocks against fp64."""
+    fsa = _fsa()
+    d, t = 128, 16
+    frames = ((1 << 31) // (2 * d) - 1) // t
+    n = frames * t
+    assert n * d * 2 < (1 << 31) <= (n + t) * d * 2
+    _say(f"case largest_head_slab: F={frames} T={t} N={n} D={d}")
+    q, k, v = synthetic.make_device_normal((1, 1, n, d), seed=11, device="cuda")
+    wl = synthetic.Workload("largest", 1, 1, d, frames, t, 0, 0)
+    dplan = fsa.DevicePlan(frames, t, 0, 0, 16, 16)
+    o, b = fsa.forward(dplan, q, k, v, wl.scale)
+    o2, b2 = fsa.forward(dplan, q, k, v, wl.scale, bound_limit=1e-30)
+    torch.cuda.synchronize()
+    assert int(b2[2].sum()) == 0
+    rng = np.random.default_rng(5)
+    sample = sorted({0, 1, 2, frames // 2, frames - 2, frames - 1, *rng.integers(0, frames, 8).tolist()})
+    qnorm, kmax = b[0][0, 0], b[1][0, 0]
+    for f in sample:
+        rows = slice(f * t, (f + 1) * t)
+        ref = _frame_reference(q, k, v, f, t, wl.scale)
+        _assert_close(synthetic.to_f64(o[:, :, rows].cpu()), ref, f"frame {f}")
+        _assert_close(synthetic.to_f64(o2[:, :, rows].cpu()), ref, f"frame {f} (online)")
+        qf = synthetic.to_f64(q[0, 0, rows].cpu())
+        kf = synthetic.to_f64(k[0, 0, rows].cpu())
+        np.testing.assert_allclose(qnorm[rows].cpu().numpy(), np.linalg.norm(qf, axis=-1), rtol=BOUND_RTOL, atol=0)
+        np.testing.assert_allclose(float(kmax[f]), np.linalg.norm(kf, axis=-1).max(), rtol=BOUND_RTOL, atol=0)
+    del q, k, v, o, o2, b, b2
+    torch.cuda.empty_cache()
