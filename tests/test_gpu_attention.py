@@ -412,3 +412,44 @@ def test_largest_head_slab():
         np.testing.assert_allclose(float(kmax[f]), np.linalg.norm(kf, axis=-1).max(), rtol=BOUND_RTOL, atol=0)
     del q, k, v, o, o2, b, b2
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------- a wider seeded sweep
+SWEEP = (_random_cases(160, 777001, prefix="sw") +
+         _random_cases(24, 777002, t_max=2048, n_max=4096, f_max=8, prefix="sww"))
+
+
+@pytest.mark.timeout(600)
+def test_random_sweep_centring_and_head_ranges():
+    """184 more seeded shapes in one test (so a failure lists them all): every
+    fifth with centred keys (some on offset keys), every second also on the
+    forced fallback, and every third with more than one head also as a call on
+    heads 1.. alone, whose rows must equal the whole call's bitwise while head 0
+    stays untouched."""
+    fails = []
+    for idx, (name, bsz, heads, d, frames, t, w, r, bq, bk, dist) in enumerate(SWEEP):
+        center = idx % 5 == 4
+        if center and dist == "normal" and idx % 10 == 9:
+            dist = "key_offset"
+        wl = synthetic.Workload(name, bsz, heads, d, frames, t, w, r, dist=dist, seed=5000 + idx)
+        _say(f"case {name}: B={bsz} H={heads} D={d} F={frames} T={t} w={w} r={r} bq={bq} bk={bk} {dist} "
+             f"center={center}")
+        try:
+            qc, kc, vc = synthetic.make_inputs(wl)
+            q, k, v = (x.cuda() for x in (qc, kc, vc))
+            ref = parity.reference(wl, qc, kc, vc)
+            o, b, dplan = _run(wl, q, k, v, bq, bk, center=center)
+            _check_bounds(wl, qc, kc, b, dplan, bq, bk, center=center)
+            _assert_close(synthetic.to_f64(o), ref, name)
+            if idx % 2 == 0:
+                o2, b2, _ = _run(wl, q, k, v, bq, bk, bound_limit=1e-30, center=center)
+                assert int(b2[2].sum()) == 0
+                _assert_close(synthetic.to_f64(o2), ref, name + " (online)")
+            if heads > 1 and idx % 3 == 0:
+                o3 = torch.zeros_like(q)
+                _run(wl, q, k, v, bq, bk, head_offset=1, head_count=heads - 1, out=o3, center=center)
+                assert torch.equal(o3[:, 1:], o[:, 1:]), "head range differs from the whole call"
+                assert not (o3[:, :1] != 0).any().item(), "a head outside the range was written"
+        except AssertionError as e:
+            fails.append(f"{name}: {str(e)[:200]}")
+    assert not fails, fails
