@@ -121,6 +121,22 @@ def test_pre_attention_random_parity(case):
     test_pre_attention_parity(case)
 
 
+SWEEP = _random_cases(150, 888001)
+
+
+@pytest.mark.timeout(600)
+def test_pre_attention_random_sweep():
+    """150 more seeded shapes of the same kind in one test (a failure lists
+    them all)."""
+    fails = []
+    for case in SWEEP:
+        try:
+            test_pre_attention_parity(case)
+        except AssertionError as e:
+            fails.append(f"{case}: {str(e)[:200]}")
+    assert not fails, fails
+
+
 def test_pre_attention_options_and_determinism():
     """Other eps and rotary base values, and bitwise-repeatable outputs."""
     wl = synthetic.PreWorkload("opt", 1, 200, 64, 2, 128, seed=9)
